@@ -1,0 +1,94 @@
+"""ctypes declarations of include/moe_layer.h (argument marshalling only).
+
+The shared library is lib/libmoe_mi355x.so inside this package, built by
+`python -m sparse_mixture_experts_layer_amd.build`.  There is no fallback: if
+the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, \
+    MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = range(8)
+MOE_F32, MOE_BF16, MOE_INT4_G32 = 0, 1, 2
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
+
+
+class MoeLayerConfig(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("num_experts", C.c_int32), ("top_k", C.c_int32),
+                ("inter", C.c_int32), ("shared_inter", C.c_int32), ("max_tokens", C.c_int32),
+                ("score", C.c_int32), ("renormalize", C.c_int32), ("routed_scale", C.c_float),
+                ("bias_mode", C.c_int32), ("act_dtype", C.c_int32), ("weight_dtype", C.c_int32)]
+
+
+class MoeWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                                           "sc_gate", "sc_up", "sc_down", "sc_s_gate", "sc_s_up",
+                                           "sc_s_down")]
+
+
+class MoeRoute(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("topk_idx", "topk_w", "topk_gap", "expert_counts",
+                                           "expert_offsets", "perm", "inv")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {status_str(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Loads the library once.  torch is imported first so that the process
+    uses a single HIP runtime (the one torch ships)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (binds libamdhip64 before the library needs it)
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"MoE HIP library not built: {LIB_PATH} is missing "
+                           "(run: python -m sparse_mixture_experts_layer_amd.build)")
+    lib = C.CDLL(LIB_PATH)
+    lib.moe_abi_version.restype = C.c_int
+    lib.moe_abi_version.argtypes = []
+    lib.moe_layer_create.restype = C.c_int
+    lib.moe_layer_create.argtypes = [C.POINTER(MoeLayerConfig), C.c_int, C.POINTER(C.c_void_p)]
+    lib.moe_layer_destroy.restype = None
+    lib.moe_layer_destroy.argtypes = [C.c_void_p]
+    lib.moe_layer_packed_bytes.restype = C.c_size_t
+    lib.moe_layer_packed_bytes.argtypes = [C.c_void_p]
+    lib.moe_layer_workspace_bytes.restype = C.c_size_t
+    lib.moe_layer_workspace_bytes.argtypes = [C.c_void_p, C.c_int32]
+    lib.moe_layer_pack_weights.restype = C.c_int
+    lib.moe_layer_pack_weights.argtypes = [C.c_void_p, C.POINTER(MoeWeights), C.c_void_p,
+                                           C.c_void_p]
+    lib.moe_layer_forward.restype = C.c_int
+    lib.moe_layer_forward.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                      C.POINTER(MoeRoute), C.c_void_p]
+    lib.moe_status_str.restype = C.c_char_p
+    lib.moe_status_str.argtypes = [C.c_int]
+    lib.moe_last_error.restype = C.c_char_p
+    lib.moe_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().moe_status_str(status).decode()
+
+
+def last_error() -> str:
+    return load().moe_last_error().decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where, last_error())

@@ -1,0 +1,353 @@
+// C ABI and host runtime of the MoE layer: configuration checks, packed-weight
+// and workspace layouts, the per-call launch plan, and error reporting.
+// Nothing here allocates device memory or synchronises the host.
+#include "../../include/moe_layer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "moe_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status_t ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+constexpr int kMaxTokens = 1 << 18;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct moe_layer {
+  moe_layer_config_t cfg;
+  int device;
+  size_t expert_bytes;   // one routed expert, packed
+  size_t shared_bytes;   // the shared expert, packed
+};
+
+namespace {
+
+size_t packed_group_bytes(const moe_layer_config_t& c, int width) {
+  const size_t wh = (size_t)width * c.hidden;
+  if (c.weight_dtype == MOE_INT4_G32) return wh + wh / 8 + wh / 2 + wh / 16;
+  return 3 * wh * 2;
+}
+
+moe_status_t check_config(const moe_layer_config_t* c) {
+  if (!c) return fail(MOE_ERR_NULL, "config is NULL");
+  if (c->act_dtype != MOE_BF16 && c->act_dtype != MOE_F32)
+    return fail(MOE_ERR_DTYPE, "act_dtype must be MOE_BF16 or MOE_F32 (got %d)", c->act_dtype);
+  if (c->weight_dtype != MOE_BF16 && c->weight_dtype != MOE_INT4_G32)
+    return fail(MOE_ERR_DTYPE, "weight_dtype must be MOE_BF16 or MOE_INT4_G32 (got %d)",
+                c->weight_dtype);
+  if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_DTYPE, "score must be MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID");
+  if (c->bias_mode != MOE_BIAS_LOGIT && c->bias_mode != MOE_BIAS_SELECT)
+    return fail(MOE_ERR_DTYPE, "bias_mode must be MOE_BIAS_LOGIT or MOE_BIAS_SELECT");
+  if (!(c->routed_scale == c->routed_scale) || c->routed_scale <= 0.f)
+    return fail(MOE_ERR_SHAPE, "routed_scale must be a positive number");
+  if (c->num_experts < 1 || c->num_experts > 512)
+    return fail(MOE_ERR_SHAPE, "num_experts must be in [1, 512] (got %d)", c->num_experts);
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->num_experts)
+    return fail(MOE_ERR_SHAPE, "top_k must be in [1, min(num_experts, 16)] (got %d)", c->top_k);
+  if (c->hidden < 64 || c->hidden % 64)
+    return fail(MOE_ERR_SHAPE, "hidden must be a positive multiple of 64 (got %d)", c->hidden);
+  if (c->inter < 32 || c->inter % 32)
+    return fail(MOE_ERR_SHAPE, "inter must be a positive multiple of 32 (got %d)", c->inter);
+  if (c->shared_inter < 0 || c->shared_inter % 32)
+    return fail(MOE_ERR_SHAPE, "shared_inter must be 0 or a multiple of 32 (got %d)",
+                c->shared_inter);
+  if (c->max_tokens < 1 || c->max_tokens > kMaxTokens)
+    return fail(MOE_ERR_SHAPE, "max_tokens must be in [1, %d] (got %d)", kMaxTokens,
+                c->max_tokens);
+  if (c->weight_dtype == MOE_INT4_G32 &&
+      (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128))
+    return fail(MOE_ERR_SHAPE, "INT4 weights need hidden, inter and shared_inter % 128 == 0");
+  return MOE_OK;
+}
+
+// Per-call plan and workspace layout.
+struct Plan {
+  int T, P, ks, tg, max_tiles, has_shared, hstride;
+  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, h, y, total;
+};
+
+Plan make_plan(const moe_layer& L, int T) {
+  const moe_layer_config_t& c = L.cfg;
+  Plan p{};
+  p.T = T;
+  p.P = T * c.top_k;
+  p.has_shared = c.shared_inter > 0;
+  // router: split H so that small batches still spread over the CUs
+  const int ne = c.num_experts <= 16 ? 1 : (c.num_experts <= 32 ? 2 : 6);
+  const int wgs = ((T + 63) / 64) * ((c.num_experts + 16 * ne - 1) / (16 * ne));
+  p.ks = 1;
+  while (wgs * p.ks < 256 && p.ks < 8 && (c.hidden / 32) % (2 * p.ks) == 0) p.ks *= 2;
+  // expert GEMM tile rows: 32 for sparse rows per expert, 64 when denser
+  const double rows_per_expert = (double)p.P / c.num_experts;
+  p.tg = rows_per_expert >= 24.0 ? 4 : 2;
+  const int bm = 16 * p.tg;
+  const int nz = c.num_experts < p.P ? c.num_experts : p.P;
+  p.max_tiles = nz + p.P / bm + (p.has_shared ? (T + bm - 1) / bm : 0) + 1;
+  const int rows = p.P + (p.has_shared ? T : 0);
+  p.hstride = c.inter > c.shared_inter ? c.inter : c.shared_inter;
+  const int E = c.num_experts;
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  p.part = take((size_t)p.ks * T * E * 4);
+  p.idx = take((size_t)p.P * 4);
+  p.w = take((size_t)p.P * 4);
+  p.gap = take((size_t)T * 4);
+  p.counts = take((size_t)(E + 1) * 4);
+  p.offsets = take((size_t)(E + 2) * 4);
+  p.perm = take((size_t)p.P * 4);
+  p.inv = take((size_t)p.P * 4);
+  p.row_tok = take((size_t)rows * 4);
+  p.tiles = take((size_t)p.max_tiles * 4);
+  p.ntiles = take(4);
+  p.h = take((size_t)rows * p.hstride * 4);
+  p.y = take((size_t)rows * c.hidden * 4);
+  p.total = o;
+  return p;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) {
+      err = hipSetDevice(dev);
+      changed = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status_t moe_layer_create(const moe_layer_config_t* cfg, int device, moe_layer_t* out) {
+  if (!out) return fail(MOE_ERR_NULL, "out handle pointer is NULL");
+  *out = nullptr;
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n == 0)
+    return fail(MOE_ERR_DEVICE, "no HIP device available (%s)",
+                e != hipSuccess ? hipGetErrorString(e) : "0 devices");
+  if (device < 0 || device >= n)
+    return fail(MOE_ERR_DEVICE, "device %d out of range (%d devices)", device, n);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MOE_ERR_DEVICE, "device %d is %s; this library is built for gfx950 only", device,
+                prop.gcnArchName);
+  moe_layer* L = new (std::nothrow) moe_layer;
+  if (!L) return fail(MOE_ERR_DEVICE, "out of host memory");
+  L->cfg = *cfg;
+  L->device = device;
+  L->expert_bytes = packed_group_bytes(*cfg, cfg->inter);
+  L->shared_bytes = cfg->shared_inter ? packed_group_bytes(*cfg, cfg->shared_inter) : 0;
+  *out = L;
+  return ok();
+}
+
+void moe_layer_destroy(moe_layer_t layer) { delete layer; }
+
+size_t moe_layer_packed_bytes(moe_layer_t L) {
+  if (!L) return 0;
+  return L->expert_bytes * (size_t)L->cfg.num_experts + L->shared_bytes;
+}
+
+size_t moe_layer_workspace_bytes(moe_layer_t L, int32_t num_tokens) {
+  if (!L || num_tokens <= 0 || num_tokens > L->cfg.max_tokens) return 0;
+  return make_plan(*L, num_tokens).total;
+}
+
+moe_status_t moe_layer_pack_weights(moe_layer_t L, const moe_weights_t* w, void* packed,
+                                    hipStream_t stream) {
+  if (!L) return fail(MOE_ERR_NULL, "layer is NULL");
+  if (!w || !packed) return fail(MOE_ERR_NULL, "weights or packed buffer is NULL");
+  const moe_layer_config_t& c = L->cfg;
+  const bool int4 = c.weight_dtype == MOE_INT4_G32;
+  const bool sh = c.shared_inter > 0;
+  if (!w->w_gate || !w->w_up || !w->w_down || (sh && (!w->s_gate || !w->s_up || !w->s_down)))
+    return fail(MOE_ERR_NULL, "a weight pointer is NULL");
+  if (int4 && (!w->sc_gate || !w->sc_up || !w->sc_down ||
+               (sh && (!w->sc_s_gate || !w->sc_s_up || !w->sc_s_down))))
+    return fail(MOE_ERR_NULL, "an INT4 scale pointer is NULL");
+  const void* ptrs[] = {w->w_gate, w->w_up, w->w_down, packed};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "weight pointers must be 16-byte aligned");
+  DeviceGuard dg(L->device);
+  if (dg.err != hipSuccess) return fail(MOE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(dg.err));
+
+  const int H = c.hidden, I = c.inter, Is = c.shared_inter, E = c.num_experts;
+  uint8_t* dst = static_cast<uint8_t*>(packed);
+  hipError_t e = hipSuccess;
+  auto pack_group = [&](const void* g, const void* u, const void* d, const void* sg,
+                        const void* su, const void* sd, int width, int batch, uint8_t* base,
+                        size_t group_bytes) -> hipError_t {
+    hipError_t r;
+    const size_t wh = (size_t)width * H;
+    if (!int4) {
+      r = moe::launch_pack_bf16((const uint16_t*)g, (const uint16_t*)u, 2, width, H, batch, wh,
+                                base, group_bytes, stream);
+      if (r != hipSuccess) return r;
+      return moe::launch_pack_bf16((const uint16_t*)d, (const uint16_t*)d, 1, H, width, batch, wh,
+                                   base + 2 * wh * 2, group_bytes, stream);
+    }
+    r = moe::launch_pack_int4((const uint8_t*)g, (const uint8_t*)u, (const uint16_t*)sg,
+                              (const uint16_t*)su, 2, width, H, batch, wh / 2, wh / 32, base,
+                              base + wh, group_bytes, stream);
+    if (r != hipSuccess) return r;
+    uint8_t* dbase = base + wh + wh / 8;
+    return moe::launch_pack_int4((const uint8_t*)d, (const uint8_t*)d, (const uint16_t*)sd,
+                                 (const uint16_t*)sd, 1, H, width, batch, wh / 2, wh / 32, dbase,
+                                 dbase + wh / 2, group_bytes, stream);
+  };
+  e = pack_group(w->w_gate, w->w_up, w->w_down, w->sc_gate, w->sc_up, w->sc_down, I, E, dst,
+                 L->expert_bytes);
+  if (e == hipSuccess && sh)
+    e = pack_group(w->s_gate, w->s_up, w->s_down, w->sc_s_gate, w->sc_s_up, w->sc_s_down, Is, 1,
+                   dst + L->expert_bytes * E, L->shared_bytes);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "pack launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+moe_status_t moe_layer_forward(moe_layer_t L, int32_t T, const void* x, const void* router_w,
+                               const float* router_bias, const void* packed, void* out,
+                               void* workspace, size_t workspace_bytes, moe_route_t* route,
+                               hipStream_t stream) {
+  if (!L) return fail(MOE_ERR_NULL, "layer is NULL");
+  const moe_layer_config_t& c = L->cfg;
+  if (T < 0 || T > c.max_tokens)
+    return fail(MOE_ERR_SHAPE, "num_tokens %d outside [0, max_tokens=%d]", T, c.max_tokens);
+  if (T == 0) {
+    if (route) memset(route, 0, sizeof *route);
+    return ok();
+  }
+  if (!x || !router_w || !packed || !out || !workspace)
+    return fail(MOE_ERR_NULL, "x, router_w, packed, out and workspace must be non-NULL");
+  const void* al[] = {x, router_w, packed, out, workspace};
+  for (const void* p : al)
+    if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (router_bias && (reinterpret_cast<uintptr_t>(router_bias) & 3u))
+    return fail(MOE_ERR_ALIGN, "router_bias must be 4-byte aligned");
+  if (out == x) return fail(MOE_ERR_SHAPE, "out may not alias x");
+  const Plan p = make_plan(*L, T);
+  if (workspace_bytes < p.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, p.total);
+  DeviceGuard dg(L->device);
+  if (dg.err != hipSuccess) return fail(MOE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(dg.err));
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + p.part);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + p.idx);
+  float* wts = reinterpret_cast<float*>(ws + p.w);
+  float* gap = reinterpret_cast<float*>(ws + p.gap);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + p.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + p.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + p.inv);
+  int32_t* row_tok = reinterpret_cast<int32_t*>(ws + p.row_tok);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + p.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + p.ntiles);
+  float* h = reinterpret_cast<float*>(ws + p.h);
+  float* y = reinterpret_cast<float*>(ws + p.y);
+  const bool f32 = c.act_dtype == MOE_F32;
+  const bool int4 = c.weight_dtype == MOE_INT4_G32;
+  const int E = c.num_experts, H = c.hidden, k = c.top_k;
+
+  hipError_t e = moe::launch_router_logits(f32, x, static_cast<const uint16_t*>(router_w), part, T,
+                                           H, E, p.ks, stream);
+  if (e == hipSuccess)
+    e = moe::launch_router_topk(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
+                                c.renormalize, c.routed_scale, idx, wts, gap, stream);
+  if (e == hipSuccess)
+    e = moe::launch_dispatch(idx, T, k, E, p.has_shared, 16 * p.tg, counts, offsets, perm, inv,
+                             row_tok, tiles, ntiles, stream);
+  moe::GemmGeom g{};
+  g.H = H;
+  g.I = c.inter;
+  g.Is = c.shared_inter;
+  g.E = E;
+  g.T = T;
+  g.expert_bytes = L->expert_bytes;
+  g.packed = static_cast<const uint8_t*>(packed);
+  g.tiles = tiles;
+  g.ntiles = ntiles;
+  g.offsets = offsets;
+  g.counts = counts;
+  g.max_tiles = p.max_tiles;
+  g.tg = p.tg;
+  if (e == hipSuccess) e = moe::launch_gateup(g, int4, f32, x, row_tok, h, p.hstride, stream);
+  if (e == hipSuccess) e = moe::launch_down(g, int4, h, p.hstride, y, stream);
+  if (e == hipSuccess)
+    e = moe::launch_combine(f32, y, H, inv, wts, k, p.P, p.has_shared, out, T, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  if (route) {
+    route->topk_idx = idx;
+    route->topk_w = wts;
+    route->topk_gap = gap;
+    route->expert_counts = counts;
+    route->expert_offsets = offsets;
+    route->perm = perm;
+    route->inv = inv;
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Expert dispatch: per-expert histogram, exclusive prefix sum and a stable
+// permutation of the (token, choice) pairs, grouped by expert and ordered by
+// token inside a group, plus the tile list the grouped GEMMs walk.
+//
+// The pages only say that a token activates a small subset of the stored
+// parameters (q4km.ai "Step-3.5-Flash", "Technical Overview"; nipponese.news
+// article, architecture section); gathering each expert's tokens into
+// contiguous rows is how the expert FFNs become dense GEMMs.
+//
+// One workgroup of 16 waves; deterministic without global atomics:
+//   1. wave w counts the pairs of its token slice per expert (LDS atomics:
+//      counts do not depend on their order);
+//   2. per expert, the wave counts are scanned in wave order, the expert
+//      totals are scanned in expert order;
+//   3. each wave walks its slice 64 tokens at a time; a pair's rank inside its
+//      expert is the number of lower lanes of the same step holding that
+//      expert (64-bit LDS masks + popcount) plus everything earlier.
+// The shared expert is group E: rows P .. P+T-1 hold tokens 0 .. T-1.
+#include "moe_common.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kDispWaves = 16;
+constexpr int kDispThreads = kDispWaves * kWave;
+
+// Exclusive scan of buf[0..n) in place (n <= kDispThreads); returns the total.
+__device__ int block_exclusive_scan(int* buf, int* tmp, int n) {
+  const int tid = threadIdx.x;
+  int v = tid < n ? buf[tid] : 0;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kDispThreads; off <<= 1) {
+    int add = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  const int total = tmp[kDispThreads - 1];
+  if (tid < n) buf[tid] = tmp[tid] - v;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int has_shared, int bm,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ row_tok, int32_t* __restrict__ tiles,
+    int32_t* __restrict__ ntiles_out) {
+  __shared__ int hist[kDispWaves][kMaxExperts];                 // 32 KiB
+  __shared__ unsigned long long mask[kDispWaves][kMaxExperts];  // 64 KiB
+  __shared__ int tot[kMaxExperts + 1];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int ntile[kMaxExperts + 1];
+  __shared__ int scan_tmp[kDispThreads];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int P = T * k;
+  const int tw = (T + kDispWaves - 1) / kDispWaves;  // tokens per wave
+  const int tbeg = min(T, wave * tw), tend = min(T, tbeg + tw);
+
+  for (int i = tid; i < kDispWaves * kMaxExperts; i += kDispThreads) {
+    (&hist[0][0])[i] = 0;
+    (&mask[0][0])[i] = 0ull;
+  }
+  __syncthreads();
+
+  // 1. histogram per wave
+  for (int t = tbeg + lane; t < tend; t += kWave) {
+    for (int j = 0; j < k; ++j) {
+      int e = idx[(size_t)t * k + j];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      atomicAdd(&hist[wave][e], 1);
+    }
+  }
+  __syncthreads();
+
+  // 2. per-expert scan over waves, then scan over experts
+  if (tid < E) {
+    int run = 0;
+    for (int w = 0; w < kDispWaves; ++w) {
+      const int c = hist[w][tid];
+      hist[w][tid] = run;
+      run += c;
+    }
+    tot[tid] = run;
+    off[tid] = run;
+  }
+  __syncthreads();
+  block_exclusive_scan(off, scan_tmp, E);
+  if (tid < E) {
+    counts[tid] = tot[tid];
+    offsets[tid] = off[tid];
+    ntile[tid] = (tot[tid] + bm - 1) / bm;
+    for (int w = 0; w < kDispWaves; ++w) hist[w][tid] += off[tid];
+  }
+  if (tid == 0) {
+    counts[E] = has_shared ? T : 0;
+    offsets[E] = P;
+    offsets[E + 1] = P + (has_shared ? T : 0);
+    ntile[E] = has_shared ? (T + bm - 1) / bm : 0;
+  }
+  __syncthreads();
+
+  // tile list: groups in order 0..E, m-tiles in order inside a group
+  const int total_tiles = block_exclusive_scan(ntile, scan_tmp, E + 1);
+  // ntile[] now holds each group's first tile; the tile count is recomputed.
+  if (tid <= E) {
+    const int c = tid < E ? tot[tid] : (has_shared ? T : 0);
+    const int nt = (c + bm - 1) / bm;
+    for (int m = 0; m < nt; ++m) tiles[ntile[tid] + m] = (tid << 16) | m;
+  }
+  if (tid == 0) ntiles_out[0] = total_tiles;
+
+  // 3. stable scatter, 64 tokens per wave step
+  const int steps = (tw + kWave - 1) / kWave;
+  for (int s = 0; s < steps; ++s) {
+    const int t = tbeg + s * kWave + lane;
+    const bool ok = t < tend;
+    int ej[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      ej[j] = 0;
+      if (j < k && ok) {
+        int e = idx[(size_t)t * k + j];
+        ej[j] = e < 0 ? 0 : (e >= E ? E - 1 : e);
+        atomicOr(&mask[wave][ej[j]], 1ull << lane);
+      }
+    }
+    __syncthreads();
+    int rank[kMaxTopK], cnt[kMaxTopK];
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      rank[j] = -1;
+      cnt[j] = 0;
+      if (j < k && ok) {
+        const unsigned long long m = mask[wave][ej[j]];
+        rank[j] = __popcll(m & below);
+        cnt[j] = __popcll(m);
+        const int row = hist[wave][ej[j]] + rank[j];
+        const int p = t * k + j;
+        perm[row] = p;
+        inv[p] = row;
+        row_tok[row] = t;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k && ok && rank[j] == 0) {
+        hist[wave][ej[j]] += cnt[j];
+        mask[wave][ej[j]] = 0ull;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (has_shared)
+    for (int t = tid; t < T; t += kDispThreads) row_tok[P + t] = t;
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s) {
+  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, idx, T, k, E, has_shared,
+                     bm, counts, offsets, perm, inv, row_tok, tiles, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,58 @@
+// Host-side launchers of the gfx950 MoE kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router: logits (fp32 partial sums over KS slices of H) + top-k ----------
+hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
+                                int T, int H, int E, int ks, hipStream_t s);
+hipError_t launch_router_topk(const float* part, int ks, const float* bias, int bias_mode, int T,
+                              int E, int k, int score, int renorm, float scale, int32_t* idx,
+                              float* w, float* gap, hipStream_t s);
+
+// ---- dispatch: counts, offsets, stable permutation, GEMM tile list ----------
+// counts/offsets have E+1 / E+2 entries (group E = shared expert, T rows).
+hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s);
+
+// ---- grouped expert GEMMs ----------------------------------------------------
+struct GemmGeom {
+  int H, I, Is, E, T;         // shapes (T = tokens of this call)
+  size_t expert_bytes;        // packed bytes of one routed expert
+  const uint8_t* packed;      // packed weights (shared expert = group E, after the routed ones)
+  const int32_t* tiles;       // tile list
+  const int32_t* ntiles;      // device scalar: number of valid tiles
+  const int32_t* offsets;     // [E+2] first permuted row of each group
+  const int32_t* counts;      // [E+1] rows of each group
+  int max_tiles;              // grid bound
+  int tg;                     // token groups of 16 per tile (tile rows = 16 * tg)
+};
+
+// h[row][f] = silu(x W_gate^T) * (x W_up^T) (fp32) for every permuted row.
+hipError_t launch_gateup(const GemmGeom& g, bool int4, bool act_f32, const void* x,
+                         const int32_t* row_tok, float* h, int hstride, hipStream_t s);
+// Y[row][:] = h[row] W_down^T (fp32; h split into bf16 hi + lo) for every permuted row.
+hipError_t launch_down(const GemmGeom& g, bool int4, const float* h, int hstride, float* y,
+                       hipStream_t s);
+
+// ---- combine: out[t] = Y[shared row of t] + sum_j w[t,j] Y[inv[t,j]] -------
+hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
+                          int k, int P, int has_shared, void* out, int T, hipStream_t s);
+
+// ---- weight packing ----------------------------------------------------------
+// bf16 [N][K] (G sources interleaved per 16-row block) -> fragments.
+hipError_t launch_pack_bf16(const uint16_t* src0, const uint16_t* src1, int G, int N, int K,
+                            int batch, size_t src_batch_stride, uint8_t* dst,
+                            size_t dst_batch_stride, hipStream_t s);
+// INT4 nibbles [N][K/2] + fp16 scales [N][K/32] -> 16x128 blocks + scale quads.
+hipError_t launch_pack_int4(const uint8_t* q0, const uint8_t* q1, const uint16_t* s0,
+                            const uint16_t* s1, int G, int N, int K, int batch,
+                            size_t q_batch_stride, size_t s_batch_stride, uint8_t* dst_q,
+                            uint8_t* dst_s, size_t dst_batch_stride, hipStream_t s);
+
+}  // namespace moe

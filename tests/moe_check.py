@@ -1,0 +1,135 @@
+"""Shared helpers of the GPU tests: run the HIP layer on seeded inputs and
+compare it with the oracle element by element.
+
+Comparison rules (tolerances per output dtype):
+  * routing: the selected experts, in rank order, must equal the oracle's for
+    every token whose oracle k-th / (k+1)-th selection-score gap is >= 1e-4
+    (a smaller gap can flip under a different fp32 summation order);
+  * dispatch: counts, offsets, perm and inv must equal the reference dispatch
+    of the GPU's own indices bit for bit;
+  * outputs: max|y_gpu - y_ref| <= tol * RMS(y_ref) over the compared tokens,
+    tol = 2e-2 for bf16 outputs, 5e-2 for INT4 weights, 1e-3 for fp32 outputs
+    (split-bf16 operands leave a relative residual below 2^-16 per product and
+    fp32 accumulation over at most a few thousand terms; 1e-3 leaves a wide
+    margin).  A token whose routing legitimately differs (near-tie) is compared
+    with the oracle re-run on the GPU's routing.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_synth
+import oracle
+
+NEAR_TIE = 1e-4
+
+
+def out_tolerance(shape) -> float:
+    if shape.weight_dtype == "int4_g32":
+        return 5e-2
+    return 1e-3 if shape.act_dtype == "f32" else 2e-2
+
+
+def expert_loader(inp):
+    """e -> (W_gate, W_up, W_down) float64 host arrays of one expert (group
+    e == E is the shared expert)."""
+    if inp.shape.weight_dtype == "int4_g32":
+        q = inp.q
+
+        def load(e):
+            return tuple(oracle.dequant_int4(q[n][0][e].cpu().numpy(), q[n][1][e].cpu().numpy())
+                         for n in ("gate", "up", "down"))
+        shared = None
+        if "s_gate" in q:
+            shared = tuple(oracle.dequant_int4(q[n][0].cpu().numpy(), q[n][1].cpu().numpy())
+                           for n in ("s_gate", "s_up", "s_down"))
+        return load, shared
+
+    def load(e):
+        return (moe_synth.host_f64(inp.w_gate[e]), moe_synth.host_f64(inp.w_up[e]),
+                moe_synth.host_f64(inp.w_down[e]))
+    shared = None
+    if inp.s_gate is not None:
+        shared = (moe_synth.host_f64(inp.s_gate), moe_synth.host_f64(inp.s_up),
+                  moe_synth.host_f64(inp.s_down))
+    return load, shared
+
+
+def run_gpu(layer, inp, tokens=None, seed_ws=None):
+    x = inp.x if tokens is None else inp.x[:tokens]
+    out, route = layer.forward(x, inp.router_w, inp.router_bias, return_route=True)
+    torch.cuda.synchronize()
+    return out, route
+
+
+def compare(inp, out, route, sample=None, score="softmax", renormalize=True, routed_scale=1.0,
+            bias_mode="logit", k=None, tokens=None):
+    """Checks one GPU forward against the oracle; returns a dict of figures."""
+    shape = inp.shape
+    k = k or shape.top_k
+    T = out.shape[0]
+    x64 = moe_synth.host_f64(inp.x[:T])
+    wr = moe_synth.host_f64(inp.router_w)
+    bias = None if inp.router_bias is None else inp.router_bias.cpu().numpy()
+    g_idx = route.topk_idx.cpu().numpy().astype(np.int64)
+    g_w = route.topk_w.cpu().numpy().astype(np.float64)
+    E = shape.experts
+
+    # dispatch: bit-exact against the reference dispatch of the GPU's own routing
+    counts, offsets, perm, inv = oracle.dispatch(g_idx, E)
+    assert np.array_equal(route.expert_counts.cpu().numpy(), counts), "expert counts differ"
+    assert np.array_equal(route.expert_offsets.cpu().numpy(), offsets), "expert offsets differ"
+    assert np.array_equal(route.perm.cpu().numpy(), perm), "permutation differs"
+    assert np.array_equal(route.inv.cpu().numpy(), inv), "inverse permutation differs"
+
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    load, shared = expert_loader(inp)
+    cache = {}
+
+    def experts(e):
+        if e not in cache:
+            cache[e] = load(e)
+        return cache[e]
+
+    y_ref, o_idx, o_w, l32 = oracle.forward(x64[rows], wr, bias, experts, shared, k, score,
+                                            renormalize, routed_scale, bias_mode)
+    sel_scores = l32
+    if bias is not None and bias_mode == "select":
+        sel_scores = (l32.astype(np.float64) + bias[None, :]).astype(np.float32)
+    gap = oracle.topk_gap(sel_scores, k)
+    exempt = gap < NEAR_TIE
+    # sets are compared; the rank order inside a set may flip on equal-ish logits
+    g_ord = np.argsort(g_idx[rows], axis=1, kind="stable")
+    o_ord = np.argsort(o_idx, axis=1, kind="stable")
+    g_sorted = np.take_along_axis(g_idx[rows], g_ord, axis=1)
+    o_sorted = np.take_along_axis(o_idx, o_ord, axis=1)
+    same = (g_sorted == o_sorted).all(axis=1)
+    bad = ~same & ~exempt
+    assert not bad.any(), (f"routing differs on {bad.sum()} non-near-tie tokens, e.g. token "
+                           f"{rows[np.argmax(bad)]}: gpu {g_idx[rows][bad][0]} oracle {o_idx[bad][0]}")
+    # weights of identically routed tokens
+    gw_s = np.take_along_axis(g_w[rows], g_ord, axis=1)
+    ow_s = np.take_along_axis(o_w, o_ord, axis=1)
+    werr = np.abs(gw_s[same] - ow_s[same]).max() if same.any() else 0.0
+    assert werr <= 1e-5, f"gate weights differ by {werr}"
+    # tokens routed differently inside the near-tie band: oracle on the GPU's routing
+    flip = ~same
+    if flip.any():
+        y_f, *_ = oracle.forward(x64[rows][flip], wr, bias, experts, shared, k, score,
+                                 renormalize, routed_scale, bias_mode, force_idx=g_idx[rows][flip])
+        y_ref = y_ref.copy()
+        y_ref[flip] = y_f
+    y_gpu = out[torch.as_tensor(rows, device=out.device)].double().cpu().numpy()
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    err = float(np.abs(y_gpu - y_ref).max())
+    tol = out_tolerance(shape)
+    res = {"max_err_over_rms": err / rms, "rms": rms, "tol": tol, "near_tie_tokens": int(exempt.sum()),
+           "flipped": int(flip.sum()), "compared_tokens": len(rows), "weight_err": float(werr)}
+    assert err <= tol * rms, f"output error {err / rms:.4g} x RMS exceeds {tol}: {res}"
+    return res
+
+
+def make_layer(shape, max_tokens=None, **kw):
+    from sparse_mixture_experts_layer_amd.layer import MoELayer
+    return MoELayer.from_shape(shape, max_tokens=max_tokens, **kw)

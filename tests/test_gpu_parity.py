@@ -1,0 +1,176 @@
+"""GPU parity: the HIP layer (through the C ABI) against the oracle.
+
+Small cases are compared on every token; the full Step-3.5-Flash shapes on
+every token where the oracle is quick (decode batches) and on a spread sample
+of tokens otherwise.  See tests/moe_check.py for the comparison rules.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from moe_check import compare, make_layer, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+W = moe_synth.WORKLOADS
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _run(shape, seed=0, tokens=None, max_tokens=None, layer_kw=None, cmp_kw=None, sample=None):
+    _say(shape.name, f"seed={seed}", f"tokens={tokens or shape.tokens}", layer_kw or "")
+    inp = moe_synth.make_layer(shape, seed=seed, device="cuda")
+    layer = make_layer(shape, max_tokens=max_tokens or shape.tokens, **(layer_kw or {}))
+    layer.pack_inputs(inp)
+    out, route = run_gpu(layer, inp, tokens)
+    res = compare(inp, out, route, sample=sample, **(cmp_kw or {}))
+    _say("ok", res)
+    return inp, layer, out, route, res
+
+
+# ----------------------------------------------------------------- tiny (fp32 activations)
+
+@pytest.mark.parametrize("tokens", [64, 1, 7, 33])
+def test_tiny_ragged(tokens):
+    _run(W["tiny"], tokens=tokens, max_tokens=64)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_tiny_seeds(seed):
+    _run(W["tiny"], seed=seed)
+
+
+def test_tiny_bf16_activations():
+    _run(W["tiny"].replace(name="tiny_bf16", act_dtype="bf16"))
+
+
+def test_tiny_no_shared_expert():
+    _run(W["tiny"].replace(name="tiny_noshared", shared_inter=0))
+
+
+@pytest.mark.parametrize("k", [1, 16])
+def test_tiny_k_extremes(k):
+    _run(W["tiny"].replace(name=f"tiny_k{k}", top_k=k))
+
+
+def test_tiny_no_renorm():
+    s = W["tiny"].replace(name="tiny_norenorm", renormalize=False)
+    _run(s, cmp_kw=dict(renormalize=False))
+
+
+@pytest.mark.parametrize("bias_mode", ["logit", "select"])
+def test_tiny_sigmoid_router_with_bias(bias_mode):
+    """The page's router configuration: sigmoid scores, a router bias,
+    renormalised weights scaled by 3."""
+    s = W["tiny"].replace(name=f"tiny_sigmoid_{bias_mode}")
+    inp = moe_synth.make_layer(s, seed=0, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    inp.router_bias = torch.randn(s.experts, generator=g, device="cuda", dtype=torch.float32)
+    _say(s.name)
+    layer = make_layer(s, score="sigmoid", routed_scale=3.0, bias_mode=bias_mode)
+    layer.pack_inputs(inp)
+    out, route = run_gpu(layer, inp)
+    res = compare(inp, out, route, score="sigmoid", routed_scale=3.0, bias_mode=bias_mode)
+    _say("ok", res)
+
+
+def test_tiny_int4():
+    s = W["tiny"].replace(name="tiny_int4", act_dtype="bf16", weight_dtype="int4_g32", inter=128,
+                          shared_inter=128)
+    _run(s)
+
+
+def test_tiny_int4_f32_activations():
+    s = W["tiny"].replace(name="tiny_int4_f32", weight_dtype="int4_g32", inter=128,
+                          shared_inter=128)
+    _run(s)
+
+
+def test_exact_ties_go_to_lower_index():
+    """Duplicated router rows give bitwise-equal logits; the lower index must win."""
+    s = W["tiny"].replace(name="tiny_ties", act_dtype="bf16")
+    inp = moe_synth.make_layer(s, seed=5, device="cuda")
+    for a, b in [(1, 9), (3, 4), (0, 15), (7, 12)]:
+        inp.router_w[b] = inp.router_w[a]
+    _say(s.name)
+    layer = make_layer(s)
+    layer.pack_inputs(inp)
+    out, route = run_gpu(layer, inp)
+    idx = route.topk_idx.cpu().numpy()
+    for a, b in [(1, 9), (3, 4), (0, 15), (7, 12)]:
+        has_a = (idx == a).any(axis=1)
+        has_b = (idx == b).any(axis=1)
+        assert not (has_b & ~has_a).any(), f"expert {b} chosen over its twin {a}"
+    assert (has_a | has_b).any()
+    compare(inp, out, route)
+
+
+def test_zero_tokens_is_noop():
+    s = W["tiny"]
+    inp = moe_synth.make_layer(s, seed=0, device="cuda")
+    layer = make_layer(s)
+    layer.pack_inputs(inp)
+    out = layer.forward(inp.x[:0], inp.router_w)
+    torch.cuda.synchronize()
+    assert out.shape == (0, s.hidden)
+
+
+def test_deterministic():
+    s = W["tiny"].replace(name="tiny_bf16", act_dtype="bf16")
+    inp = moe_synth.make_layer(s, seed=0, device="cuda")
+    layer = make_layer(s)
+    layer.pack_inputs(inp)
+    o1, r1 = run_gpu(layer, inp)
+    o2, r2 = run_gpu(layer, inp)
+    assert torch.equal(o1, o2)
+    assert torch.equal(r1.perm, r2.perm) and torch.equal(r1.topk_idx, r2.topk_idx)
+
+
+def test_argument_errors():
+    from sparse_mixture_experts_layer_amd import _binding as B
+    s = W["tiny"]
+    inp = moe_synth.make_layer(s, seed=0, device="cuda")
+    layer = make_layer(s, max_tokens=32)
+    layer.pack_inputs(inp)
+    with pytest.raises(B.MoeError) as e:   # T > max_tokens
+        layer.forward(inp.x, inp.router_w)
+    assert e.value.status == B.MOE_ERR_SHAPE
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.MoeError) as e:
+        layer.forward(inp.x[:8], inp.router_w, workspace=ws)
+    assert e.value.status == B.MOE_ERR_WORKSPACE
+
+
+# ----------------------------------------------------------------- full Step-3.5-Flash shapes
+
+def _spread(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    pick = set([0, T - 1, T // 2]) | set(rng.choice(T, size=n, replace=False).tolist())
+    return sorted(pick)
+
+
+def test_decode_32():
+    _run(W["decode"])
+
+
+def test_verify_256_zipf():
+    _, _, _, route, _ = _run(W["verify"], sample=_spread(256, 40))
+    counts = route.expert_counts.cpu().numpy()
+    assert counts.max() > 150 and (counts > 0).sum() > 200   # skewed and wide
+
+
+def test_prefill_16384_sampled():
+    _run(W["prefill"], sample=_spread(16384, 24))
+
+
+def test_int4_decode_32():
+    _run(W["int4_decode"])
+
+
+@pytest.mark.parametrize("tokens", [1, 5, 17])
+def test_decode_ragged(tokens):
+    _run(W["decode"], tokens=tokens, max_tokens=32)
