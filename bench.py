@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE FFN layer (Step-3.5-Flash shape) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+One step = one moe_layer_forward over one batch of synthetic tokens (router,
+dispatch, gate/up GEMM, down GEMM, combine), with every input already resident
+in HBM.  W untimed steps, then K timed steps between two device
+synchronisations; per-stage durations come from HIP events the library records
+on its own stream during those same K steps.  Prints one JSON line.
+
+Workloads (seeded synthetic inputs, shapes from the llm-atlas "Step-3.5-Flash"
+config fields): decode (32 tokens, default), verify (256 tokens, Zipf expert
+popularity), prefill (16384 tokens), int4_decode (32 tokens, INT4-g32 weights),
+tiny (parity-sized).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % of HBM BW (decode) / % of bf16 MFMA peak (prefill)"
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E (published)
+PEAK_BF16 = 2.5e15         # flop/s, MI355X dense bf16 MFMA (published)
+PROFILES = os.path.join(ROOT, "profiles")
+GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_layer_amd", "csrc", "moe_gemm_stream.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "verify", "prefill", "int4_decode"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the oracle on the host (e.g. under a profiler)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def src_digest(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_counters(workload: str):
+    """HBM traffic of the gate/up kernel from committed rocprofv3 --pmc runs.
+
+    profiles/gate_up_<workload>_counters.txt holds 'key: value' lines, among
+    them src_sha (digest of the kernel source the counters were taken on) and
+    fetch_bytes / write_bytes per launch already scaled by the copy-kernel
+    calibration.  Returns None when absent or taken on other kernel code."""
+    path = os.path.join(PROFILES, f"gate_up_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("src_sha") != src_digest(GEMM_SRC):
+        return None
+    try:
+        return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, shape, target_s: float):
+    """The oracle as it stands, on the host cores, on the first S tokens of the
+    same batch (S doubled until the run takes about target_s seconds)."""
+    import numpy as np
+    import torch
+    import threadpoolctl
+    import moe_synth
+    import oracle
+
+    E = shape.experts
+    x64 = moe_synth.host_f64(inp.x)
+    wr = moe_synth.host_f64(inp.router_w)
+    bias = None if inp.router_bias is None else inp.router_bias.cpu().numpy()
+    int4 = shape.weight_dtype == "int4_g32"
+    host = {}
+
+    def fetch(e):        # device -> host copy, outside the timed region
+        if e in host:
+            return
+        if int4:
+            host[e] = tuple((inp.q[n][0][e].cpu().numpy(), inp.q[n][1][e].cpu().numpy())
+                            for n in ("gate", "up", "down"))
+        else:
+            host[e] = (inp.w_gate[e].cpu(), inp.w_up[e].cpu(), inp.w_down[e].cpu())
+
+    def experts(e):      # widening to float64 is part of the oracle's work
+        if int4:
+            return tuple(oracle.dequant_int4(q, s) for q, s in host[e])
+        return tuple(t.to(torch.float64).numpy() for t in host[e])
+
+    if int4:
+        shared = tuple(oracle.dequant_int4(inp.q[n][0].cpu().numpy(), inp.q[n][1].cpu().numpy())
+                       for n in ("s_gate", "s_up", "s_down"))
+    else:
+        shared = tuple(moe_synth.host_f64(t) for t in (inp.s_gate, inp.s_up, inp.s_down))
+    info = threadpoolctl.threadpool_info()
+    cores = max([d.get("num_threads", 1) for d in info] or [1])
+    T = x64.shape[0]
+    s, elapsed = 1, 0.0
+    while True:
+        idx, *_ = oracle.route(x64[:s], wr, bias, shape.top_k)
+        for e in np.unique(idx):
+            fetch(int(e))
+        t0 = time.perf_counter()
+        oracle.forward(x64[:s], wr, bias, experts, shared, shape.top_k)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= target_s or s >= T:
+            break
+        s = min(T, s * 2 if elapsed < target_s / 4 else max(s + 1, int(s * target_s / elapsed)))
+        host.clear()
+    return {"value": s / elapsed, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {s} of the {T} tokens of the same batch (float64 NumPy oracle, "
+                      f"{elapsed:.1f} s; expert weights widened one expert at a time)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is designed, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_synth
+    from sparse_mixture_experts_layer_amd import _binding as B
+    from sparse_mixture_experts_layer_amd.layer import MoELayer
+
+    shape = moe_synth.WORKLOADS[args.workload]
+    T, H, E, k, I, Is = (shape.tokens, shape.hidden, shape.experts, shape.top_k, shape.inter,
+                         shape.shared_inter)
+    log(f"[bench] workload {args.workload}: T={T} H={H} E={E} k={k} I={I} Is={Is} "
+        f"weights={shape.weight_dtype}")
+    t0 = time.time()
+    inp = moe_synth.make_layer(shape, seed=args.seed, device="cuda")
+    layer = MoELayer.from_shape(shape)
+    layer.pack_inputs(inp)
+    out = torch.empty((T, H), dtype=inp.x.dtype, device="cuda")
+    ws = torch.empty(layer.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs + packing ready in {time.time() - t0:.1f}s "
+        f"(packed {layer.packed_bytes / 1e9:.2f} GB, workspace {ws.numel() / 1e6:.1f} MB)")
+
+    for _ in range(args.warmup):
+        layer.forward(inp.x, inp.router_w, inp.router_bias, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ev = B.StageEvents(sets=args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.forward(inp.x, inp.router_w, inp.router_bias, out=out, workspace=ws,
+                      stage_events=ev, event_set=i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    stages = [ev.stage_ms(i) for i in range(args.steps)]
+    stage_avg = [sum(s[j] for s in stages) / len(stages) for j in range(len(B.STAGES))]
+    log("[bench] stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in zip(B.STAGES, stage_avg)))
+
+    # routing of the (deterministic) batch: distinct experts touched
+    _, route = layer.forward(inp.x, inp.router_w, inp.router_bias, out=out, workspace=ws,
+                             return_route=True)
+    counts = route.expert_counts.cpu()
+    U = int((counts > 0).sum())
+    P = T * k
+    int4 = shape.weight_dtype == "int4_g32"
+    wb = 0.5 + 2.0 / 32 if int4 else 2.0          # bytes per weight (INT4: nibble + fp16/32)
+    ab = 4 if shape.act_dtype == "f32" else 2
+    expert_b = 3 * I * H * wb
+    b_alg = U * expert_b + 3 * Is * H * wb + E * H * 2 + 2 * T * H * ab
+    f_alg = T * (2 * H * E + k * 6 * H * I + 6 * H * Is)
+    t_layer = ms / 1e3
+    gu_ms = stage_avg[2]
+    if args.workload == "prefill":
+        gu_flops = 4.0 * H * (P * I + T * Is)
+        achieved = gu_flops / (gu_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_BF16, 4),
+                "traffic": read_counters(args.workload)}
+        layer_frac = {"mfma_frac": round(f_alg / t_layer / PEAK_BF16, 4)}
+    else:
+        gu_bytes = (U * 2 * I * H + 2 * Is * H) * wb + T * H * ab + (P + T) * I * 2
+        achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(achieved * 1e9 / PEAK_HBM, 4),
+                "traffic": read_counters(args.workload)}
+        layer_frac = {"hbm_frac": round(b_alg / t_layer / PEAK_HBM, 4)}
+    roof["kernel"] = "gate_up (grouped gate/up GEMM + SiLU*up)"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host ...")
+        cpu = cpu_baseline(inp, shape, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu}")
+
+    wl_desc = {"tiny": "tiny parity layer", "decode": "Step-3.5-Flash MoE layer, decode batch",
+               "verify": "Step-3.5-Flash MoE layer, MTP verify batch (64 streams x 4), Zipf experts",
+               "prefill": "Step-3.5-Flash MoE layer, prefill chunk",
+               "int4_decode": "Step-3.5-Flash MoE layer, decode batch, INT4-g32 weights"}
+    line = {
+        "metric": METRIC,
+        "value": round(T / t_layer, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not int4 else "bf16 x int4-g32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": f"{args.workload}: {wl_desc[args.workload]}", "tokens": T,
+                   "hidden": H, "experts": E, "top_k": k, "expert_inter": I,
+                   "shared_inter": Is, "weights": shape.weight_dtype,
+                   "routing": shape.routing, "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {**layer_frac, "alg_bytes": int(b_alg), "alg_flops": int(f_alg),
+                  "experts_touched": U,
+                  "stage_ms": {n: round(v, 5) for n, v in zip(B.STAGES, stage_avg)}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

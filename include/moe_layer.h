@@ -163,6 +163,22 @@ moe_status_t moe_layer_forward(moe_layer_t layer, int32_t num_tokens, const void
                                const void* packed, void* out, void* workspace,
                                size_t workspace_bytes, moe_route_t* route, hipStream_t stream);
 
+/* Number of events moe_layer_forward_timed records. */
+#define MOE_STAGE_EVENTS 6
+
+/* moe_layer_forward, and on `stream` also records stage_events[0] before the
+ * router and stage_events[1..5] after the router (logits + top-k), dispatch,
+ * gate/up GEMM, down GEMM and combine stages, so that
+ * hipEventElapsedTime(stage_events[i], stage_events[i+1]) is the duration of
+ * stage i.  stage_events holds MOE_STAGE_EVENTS events created by the caller
+ * (hipEventCreate); the same errors as moe_layer_forward, plus MOE_ERR_NULL
+ * for a NULL array. */
+moe_status_t moe_layer_forward_timed(moe_layer_t layer, int32_t num_tokens, const void* x,
+                                     const void* router_w, const float* router_bias,
+                                     const void* packed, void* out, void* workspace,
+                                     size_t workspace_bytes, moe_route_t* route,
+                                     hipStream_t stream, hipEvent_t* stage_events);
+
 /* Short constant name of a status code. */
 const char* moe_status_str(moe_status_t status);
 

@@ -16,6 +16,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKS
 MOE_F32, MOE_BF16, MOE_INT4_G32 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
+MOE_STAGE_EVENTS = 6
+STAGES = ("router", "dispatch", "gate_up", "down", "combine")
 
 
 class MoeLayerConfig(C.Structure):
@@ -73,6 +75,8 @@ def load() -> C.CDLL:
     lib.moe_layer_forward.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                       C.POINTER(MoeRoute), C.c_void_p]
+    lib.moe_layer_forward_timed.restype = C.c_int
+    lib.moe_layer_forward_timed.argtypes = lib.moe_layer_forward.argtypes + [C.c_void_p]
     lib.moe_status_str.restype = C.c_char_p
     lib.moe_status_str.argtypes = [C.c_int]
     lib.moe_last_error.restype = C.c_char_p
@@ -92,3 +96,48 @@ def last_error() -> str:
 def check(status: int, where: str) -> None:
     if status != MOE_OK:
         raise MoeError(status, where, last_error())
+
+
+class StageEvents:
+    """Sets of MOE_STAGE_EVENTS HIP events for moe_layer_forward_timed (one set
+    per call, so back-to-back calls can be read afterwards), created and read
+    through the HIP runtime the process already loaded (torch's)."""
+
+    def __init__(self, sets: int = 1):
+        load()
+        self.hip = C.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.sets = sets
+        self.array = (C.c_void_p * (MOE_STAGE_EVENTS * sets))()
+        for i in range(MOE_STAGE_EVENTS * sets):
+            ev = C.c_void_p()
+            if self.hip.hipEventCreate(C.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.array[i] = ev
+
+    def ptr(self, s: int = 0) -> int:
+        """Address of event set s (a hipEvent_t[MOE_STAGE_EVENTS])."""
+        return C.addressof(self.array) + s * MOE_STAGE_EVENTS * C.sizeof(C.c_void_p)
+
+    def stage_ms(self, s: int = 0):
+        """Durations (ms) of the 5 stages recorded in set s (synchronises)."""
+        base = s * MOE_STAGE_EVENTS
+        self.hip.hipEventSynchronize(self.array[base + MOE_STAGE_EVENTS - 1])
+        out = []
+        for i in range(MOE_STAGE_EVENTS - 1):
+            ms = C.c_float()
+            if self.hip.hipEventElapsedTime(C.byref(ms), self.array[base + i],
+                                            self.array[base + i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def __del__(self):
+        try:
+            for i in range(MOE_STAGE_EVENTS * self.sets):
+                self.hip.hipEventDestroy(self.array[i])
+        except Exception:
+            pass

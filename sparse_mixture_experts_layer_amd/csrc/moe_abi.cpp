@@ -267,10 +267,14 @@ moe_status_t moe_layer_pack_weights(moe_layer_t L, const moe_weights_t* w, void*
   return ok();
 }
 
-moe_status_t moe_layer_forward(moe_layer_t L, int32_t T, const void* x, const void* router_w,
-                               const float* router_bias, const void* packed, void* out,
-                               void* workspace, size_t workspace_bytes, moe_route_t* route,
-                               hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* router_w,
+                          const float* router_bias, const void* packed, void* out,
+                          void* workspace, size_t workspace_bytes, moe_route_t* route,
+                          hipStream_t stream, hipEvent_t* ev) {
   if (!L) return fail(MOE_ERR_NULL, "layer is NULL");
   const moe_layer_config_t& c = L->cfg;
   if (T < 0 || T > c.max_tokens)
@@ -311,14 +315,19 @@ moe_status_t moe_layer_forward(moe_layer_t L, int32_t T, const void* x, const vo
   const bool int4 = c.weight_dtype == MOE_INT4_G32;
   const int E = c.num_experts, H = c.hidden, k = c.top_k;
 
-  hipError_t e = moe::launch_router_logits(f32, x, static_cast<const uint16_t*>(router_w), part, T,
-                                           H, E, p.ks, stream);
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (e == hipSuccess)
+    e = moe::launch_router_logits(f32, x, static_cast<const uint16_t*>(router_w), part, T, H, E,
+                                  p.ks, stream);
   if (e == hipSuccess)
     e = moe::launch_router_topk(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
                                 c.renormalize, c.routed_scale, idx, wts, gap, stream);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = moe::launch_dispatch(idx, T, k, E, p.has_shared, 16 * p.tg, counts, offsets, perm, inv,
                              row_tok, tiles, ntiles, stream);
+  if (e == hipSuccess) e = mark(2);
   moe::GemmGeom g{};
   g.H = H;
   g.I = c.inter;
@@ -334,9 +343,12 @@ moe_status_t moe_layer_forward(moe_layer_t L, int32_t T, const void* x, const vo
   g.max_tiles = p.max_tiles;
   g.tg = p.tg;
   if (e == hipSuccess) e = moe::launch_gateup(g, int4, f32, x, row_tok, h, p.hstride, stream);
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = moe::launch_down(g, int4, h, p.hstride, y, stream);
+  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
     e = moe::launch_combine(f32, y, H, inv, wts, k, p.P, p.has_shared, out, T, stream);
+  if (e == hipSuccess) e = mark(5);
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   if (route) {
     route->topk_idx = idx;
@@ -348,6 +360,28 @@ moe_status_t moe_layer_forward(moe_layer_t L, int32_t T, const void* x, const vo
     route->inv = inv;
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_layer_forward(moe_layer_t L, int32_t T, const void* x, const void* router_w,
+                               const float* router_bias, const void* packed, void* out,
+                               void* workspace, size_t workspace_bytes, moe_route_t* route,
+                               hipStream_t stream) {
+  return forward_impl(L, T, x, router_w, router_bias, packed, out, workspace, workspace_bytes,
+                      route, stream, nullptr);
+}
+
+moe_status_t moe_layer_forward_timed(moe_layer_t L, int32_t T, const void* x,
+                                     const void* router_w, const float* router_bias,
+                                     const void* packed, void* out, void* workspace,
+                                     size_t workspace_bytes, moe_route_t* route,
+                                     hipStream_t stream, hipEvent_t* stage_events) {
+  if (!stage_events) return fail(MOE_ERR_NULL, "stage_events is NULL");
+  return forward_impl(L, T, x, router_w, router_bias, packed, out, workspace, workspace_bytes,
+                      route, stream, stage_events);
 }
 
 }  // extern "C"

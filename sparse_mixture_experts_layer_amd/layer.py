@@ -157,7 +157,10 @@ class MoELayer:
     def forward(self, x: torch.Tensor, router_w: torch.Tensor,
                 router_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, packed: Optional[torch.Tensor] = None,
-                return_route: bool = False):
+                return_route: bool = False, stage_events: Optional["B.StageEvents"] = None,
+                event_set: int = 0):
+        """y = layer(x).  With stage_events (a _binding.StageEvents) the call goes
+        through moe_layer_forward_timed and records event set `event_set`."""
         c = self.cfg
         T = x.shape[0]
         dev = self.device
@@ -175,10 +178,14 @@ class MoELayer:
         if workspace is None:
             workspace = torch.empty(max(self.workspace_bytes(T), 1), dtype=torch.uint8, device=dev)
         route = B.MoeRoute()
-        B.check(self.lib.moe_layer_forward(self._h, T, x.data_ptr(), router_w.data_ptr(),
-                                           _ptr(router_bias), packed.data_ptr(), out.data_ptr(),
-                                           workspace.data_ptr(), workspace.numel(),
-                                           C.byref(route), self._stream()), "moe_layer_forward")
+        args = (self._h, T, x.data_ptr(), router_w.data_ptr(), _ptr(router_bias),
+                packed.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                C.byref(route), self._stream())
+        if stage_events is None:
+            B.check(self.lib.moe_layer_forward(*args), "moe_layer_forward")
+        else:
+            B.check(self.lib.moe_layer_forward_timed(*args, stage_events.ptr(event_set)),
+                    "moe_layer_forward_timed")
         if not return_route:
             return out
         return out, self._route_views(route, workspace, T)
