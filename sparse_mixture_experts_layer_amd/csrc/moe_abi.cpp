@@ -105,9 +105,11 @@ Plan make_plan(const moe_layer& L, int T) {
   const int wgs = ((T + 63) / 64) * ((c.num_experts + 16 * ne - 1) / (16 * ne));
   p.ks = 1;
   while (wgs * p.ks < 256 && p.ks < 8 && (c.hidden / 32) % (2 * p.ks) == 0) p.ks *= 2;
-  // expert GEMM tile rows: 32 for sparse rows per expert, 64 when denser
+  // expert GEMM tile rows: 16 when experts see about one row (decode), 32 or
+  // 64 when denser
   const double rows_per_expert = (double)p.P / c.num_experts;
-  p.tg = rows_per_expert >= 24.0 ? 4 : 2;
+  p.tg = rows_per_expert < 2.0 ? 1 : (rows_per_expert < 24.0 ? 2 : 4);
+  if (c.weight_dtype == MOE_INT4_G32 && p.tg > 2) p.tg = 2;  // register budget
   const int bm = 16 * p.tg;
   const int nz = c.num_experts < p.P ? c.num_experts : p.P;
   p.max_tiles = nz + p.P / bm + (p.has_shared ? (T + bm - 1) / bm : 0) + 1;
@@ -243,20 +245,20 @@ moe_status_t moe_layer_pack_weights(moe_layer_t L, const moe_weights_t* w, void*
     hipError_t r;
     const size_t wh = (size_t)width * H;
     if (!int4) {
-      r = moe::launch_pack_bf16((const uint16_t*)g, (const uint16_t*)u, 2, width, H, batch, wh,
+      r = moe::launch_pack_bf16((const uint16_t*)g, (const uint16_t*)u, 2, 2, width, H, batch, wh,
                                 base, group_bytes, stream);
       if (r != hipSuccess) return r;
-      return moe::launch_pack_bf16((const uint16_t*)d, (const uint16_t*)d, 1, H, width, batch, wh,
-                                   base + 2 * wh * 2, group_bytes, stream);
+      return moe::launch_pack_bf16((const uint16_t*)d, (const uint16_t*)d, 1, 4, H, width, batch,
+                                   wh, base + 2 * wh * 2, group_bytes, stream);
     }
     r = moe::launch_pack_int4((const uint8_t*)g, (const uint8_t*)u, (const uint16_t*)sg,
-                              (const uint16_t*)su, 2, width, H, batch, wh / 2, wh / 32, base,
+                              (const uint16_t*)su, 2, 2, width, H, batch, wh / 2, wh / 32, base,
                               base + wh, group_bytes, stream);
     if (r != hipSuccess) return r;
     uint8_t* dbase = base + wh + wh / 8;
     return moe::launch_pack_int4((const uint8_t*)d, (const uint8_t*)d, (const uint16_t*)sd,
-                                 (const uint16_t*)sd, 1, H, width, batch, wh / 2, wh / 32, dbase,
-                                 dbase + wh / 2, group_bytes, stream);
+                                 (const uint16_t*)sd, 1, 4, H, width, batch, wh / 2, wh / 32,
+                                 dbase, dbase + wh / 2, group_bytes, stream);
   };
   e = pack_group(w->w_gate, w->w_up, w->w_down, w->sc_gate, w->sc_up, w->sc_down, I, E, dst,
                  L->expert_bytes);

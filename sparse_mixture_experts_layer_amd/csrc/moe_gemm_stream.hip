@@ -7,28 +7,33 @@
 // SiLU gating is the reading taken for the swiglu fields, whose limit is 0
 // (no clamp) on every MoE layer.
 //
-// Work unit: one tile of up to 16*TG rows of one group x 64 output features
-// (4 waves x 16).  Weights are the MFMA A operand (their rows land on C rows),
-// the tile's rows the B operand, so the weight stream is one 1 KiB coalesced
-// fragment per wave per 32-k step no matter how few tokens an expert has -- the
-// decode regime, where nearly every byte moved is an expert weight.  Weight
-// fragments are prefetched a group of U steps ahead (double buffer).
+// Work unit: one tile of up to 16*TG rows of one group x the output features
+// of 4 waves.  The tile's rows are the MFMA A operand and the weights the B
+// operand, so a lane's four C values belong to one weight row (one INT4 scale
+// per k-group) and four token rows.  Every wave streams one contiguous 4 KiB
+// block of packed weights per 32-k step (bf16: gate f, gate f+16, up f, up f+16
+// for gate/up; four 16-row blocks for down), no matter how few rows an expert
+// has -- the decode regime, where nearly every byte moved is an expert weight.
+// Weights and activations of the next group of k-steps are in flight while the
+// current group is multiplied.
 //
-// INT4 (group 32): each lane's 16 bytes hold 4 k-groups x 8 nibbles of one
-// row; they widen to exact bf16 values 136+q, one MFMA against -136 per
-// k-group removes the offset, and each group's fp32 partial is multiplied by
-// its fp16 scale before it joins the accumulator, so the only rounding beyond
-// the fp32 sums is none: s*q is never formed in a narrower type.
+// INT4 (group 32): one 4 KiB block covers 128 k; each lane's 16 bytes hold
+// 4 k-groups x 8 nibbles of one row and widen to exact bf16 values 136+q; an
+// MFMA of the activations against -136 (shared by the four weight blocks of a
+// k-group) removes the offset, and each group's fp32 partial is multiplied by
+// its fp16 scale before it joins the accumulator.
 #include "moe_common.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
 namespace {
 
-// B operand source: bf16 rows (one 16-byte load per 32-k step) or fp32 rows
-// (two loads, split into bf16 hi + lo and issued as two MFMAs).
+constexpr int kBlockBytes = 4 * kFragBytes;  // one wave's weights per k-step
+
+// A operand (16 rows x 32 k) from bf16 rows (one 16-byte load) or fp32 rows
+// (two loads).  fp32 rows enter as bf16 hi + lo (SPLIT) or rounded to bf16.
 template <bool F32>
-struct BRow {
+struct ARow {
   static constexpr int kLoads = F32 ? 2 : 1;
   u32x4 v[kLoads];
   __device__ __forceinline__ void load(const void* base, size_t elem_off, bool ok) {
@@ -60,10 +65,11 @@ struct BRow {
   }
 };
 
-template <bool F32>
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 bhi, bf16x8 blo, f32x4 c) {
-  c = mfma16(a, bhi, c);
-  if (F32) c = mfma16(a, blo, c);
+// c += A * B, A given as hi (+ lo when SPLIT).
+template <bool SPLIT>
+__device__ __forceinline__ f32x4 mma(bf16x8 ahi, bf16x8 alo, bf16x8 b, f32x4 c) {
+  c = mfma16(ahi, b, c);
+  if (SPLIT) c = mfma16(alo, b, c);
   return c;
 }
 
@@ -83,402 +89,314 @@ __device__ __forceinline__ bool tile_info(const GemmGeom& g, int tile, TileInfo&
   return ti.nrows > 0;
 }
 
-// ------------------------------------------------------------------ bf16 gate/up
-template <bool F32, int TG, int U>
-__global__ __launch_bounds__(256) void gateup_bf16_kernel(GemmGeom g, const void* __restrict__ x,
+// Rows of the A operand: lane (l % 16) of token group t reads row t*16 + l%16.
+template <int TG>
+struct TileRows {
+  size_t off[TG];
+  bool ok[TG];
+  // gathered activation rows (token ids via row_tok), row stride H
+  __device__ __forceinline__ void gather(const TileInfo& ti, const int32_t* row_tok, int T, int H,
+                                         int lane) {
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const int r = t * 16 + (lane & 15);
+      ok[t] = r < ti.nrows;
+      int tok = ok[t] ? row_tok[ti.row0 + r] : 0;
+      tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
+      off[t] = (size_t)tok * H + (lane >> 4) * 8;
+    }
+  }
+  // contiguous rows of a permuted buffer, row stride `stride`
+  __device__ __forceinline__ void direct(const TileInfo& ti, int stride, int lane) {
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const int r = t * 16 + (lane & 15);
+      ok[t] = r < ti.nrows;
+      off[t] = (size_t)(ti.row0 + (ok[t] ? r : 0)) * stride + (lane >> 4) * 8;
+    }
+  }
+};
+
+// ------------------------------------------------------------------ bf16 weights
+// MODE 0: gate/up (A = gathered x, fp32 or bf16; out h fp32 with SiLU*up)
+// MODE 1: down    (A = h fp32 split hi+lo; out Y fp32)
+// Packed block of a wave: gate/up [W/32][H/32][g0 g1 u0 u1]; down [H/64][W/32][f0..f3].
+template <int MODE, bool XF32, int TG, int U>
+__global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void* __restrict__ a_src,
                                                           const int32_t* __restrict__ row_tok,
-                                                          int T, float* __restrict__ hout,
-                                                          int hstride, int nblk) {
+                                                          float* __restrict__ out, int hstride,
+                                                          int nblk) {
+  constexpr bool AF32 = MODE == 1 ? true : XF32;
+  constexpr bool SPLIT = AF32;  // fp32 A rows always enter as hi + lo
   const int tile = blockIdx.x / nblk, nb = blockIdx.x % nblk;
   TileInfo ti;
   if (!tile_info(g, tile, ti)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int f0 = nb * 64 + wave * 16;
-  if (f0 >= ti.width) return;
-  const int H = g.H, nk = H / 32;
-  const uint8_t* wp = g.packed + (size_t)ti.group * g.expert_bytes +
-                      (size_t)(f0 / 16) * nk * 2 * kFragBytes + lane * 16;
-
-  size_t xoff[TG];
-  bool ok[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    const int r = t * 16 + (lane & 15);
-    ok[t] = r < ti.nrows;
-    int tok = ok[t] ? row_tok[ti.row0 + r] : 0;
-    tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
-    xoff[t] = (size_t)tok * H + (lane >> 4) * 8;
+  const int H = g.H;
+  int f0, K;
+  const uint8_t* wp = g.packed + (size_t)ti.group * g.expert_bytes + lane * 16;
+  TileRows<TG> rows;
+  if (MODE == 0) {
+    f0 = nb * 128 + wave * 32;
+    if (f0 >= ti.width) return;
+    K = H;
+    wp += (size_t)(f0 / 32) * (K / 32) * kBlockBytes;
+    rows.gather(ti, row_tok, g.T, H, lane);
+  } else {
+    f0 = nb * 256 + wave * 64;
+    if (f0 >= H) return;
+    K = ti.width;
+    wp += (size_t)2 * ti.width * H * 2 + (size_t)(f0 / 64) * (K / 32) * kBlockBytes;
+    rows.direct(ti, hstride, lane);
   }
+  const int nk = K / 32;
 
-  f32x4 accg[TG], accu[TG];
+  f32x4 acc[TG][4];
 #pragma unroll
-  for (int t = 0; t < TG; ++t) accg[t] = accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TG; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 wa[U][2], wn[U][2];
+  u32x4 w[U][4], wn[U][4];
+  ARow<AF32> a[U][TG], an[U][TG];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    wa[u][0] = load16_stream(wp + (size_t)u * 2 * kFragBytes);
-    wa[u][1] = load16_stream(wp + (size_t)u * 2 * kFragBytes + kFragBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[u][j] = load16_stream(wp + (size_t)u * kBlockBytes + j * kFragBytes);
+#pragma unroll
+    for (int t = 0; t < TG; ++t) a[u][t].load(a_src, rows.off[t] + u * 32, rows.ok[t]);
   }
   for (int k0 = 0; k0 < nk; k0 += U) {
-    BRow<F32> b[U][TG];
+    const bool more = k0 + U < nk;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          wn[u][j] = load16_stream(wp + (size_t)(k0 + U + u) * kBlockBytes + j * kFragBytes);
+#pragma unroll
+        for (int t = 0; t < TG; ++t)
+          an[u][t].load(a_src, rows.off[t] + (size_t)(k0 + U + u) * 32, rows.ok[t]);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int t = 0; t < TG; ++t) b[u][t].load(x, xoff[t] + (size_t)(k0 + u) * 32, ok[t]);
-    const bool more = k0 + U < nk;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (more) {
-        wn[u][0] = load16_stream(wp + (size_t)(k0 + U + u) * 2 * kFragBytes);
-        wn[u][1] = load16_stream(wp + (size_t)(k0 + U + u) * 2 * kFragBytes + kFragBytes);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
       for (int t = 0; t < TG; ++t) {
-        bf16x8 bh, bl;
-        b[u][t].operands(bh, bl);
-        accg[t] = mma<F32>(as_bf16x8(wa[u][0]), bh, bl, accg[t]);
-        accu[t] = mma<F32>(as_bf16x8(wa[u][1]), bh, bl, accu[t]);
-      }
-    }
+        bf16x8 ah, al;
+        a[u][t].operands(ah, al);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      wa[u][0] = wn[u][0];
-      wa[u][1] = wn[u][1];
+        for (int j = 0; j < 4; ++j) acc[t][j] = mma<SPLIT>(ah, al, as_bf16x8(w[u][j]), acc[t][j]);
+      }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[u][j] = wn[u][j];
+#pragma unroll
+        for (int t = 0; t < TG; ++t) a[u][t] = an[u][t];
+      }
     }
   }
 
-  // epilogue: lane holds features f0 + 4*(lane/16) + i of row (lane % 16)
+  // epilogue: lane holds rows t*16 + 4*(lane/16) + i of weight column (lane % 16)
 #pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    if (!ok[t]) continue;
-    const size_t row = (size_t)ti.row0 + t * 16 + (lane & 15);
-    const int f = f0 + (lane >> 4) * 4;
-    f32x4 hv;
+  for (int t = 0; t < TG; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hv[i] = silu(accg[t][i]) * accu[t][i];
-    *reinterpret_cast<f32x4*>(hout + row * hstride + f) = hv;
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int r = t * 16 + (lane >> 4) * 4 + i;
+      if (r >= ti.nrows) continue;
+      const size_t row = (size_t)ti.row0 + r;
+      if (MODE == 0) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          out[row * hstride + f0 + f * 16 + (lane & 15)] = silu(acc[t][f][i]) * acc[t][2 + f][i];
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) out[row * H + f0 + f * 16 + (lane & 15)] = acc[t][f][i];
+      }
+    }
 }
 
-// ------------------------------------------------------------------ bf16 down
-template <int TG, int U>
-__global__ __launch_bounds__(256) void down_bf16_kernel(GemmGeom g, const float* __restrict__ h,
-                                                        int hstride, float* __restrict__ y,
-                                                        int nblk) {
+// ------------------------------------------------------------------ INT4 weights
+// Per group of width W:
+//   gate/up q      [W/32][H/128][g0 g1 u0 u1][64 lanes][16 B]      W*H bytes
+//   gate/up scales [W/32][H/128][16 rows][4 blocks][4 kg] fp16     W*H/8 bytes
+//   down q         [H/64][W/128][f0..f3][64][16 B]                 H*W/2 bytes
+//   down scales    [H/64][W/128][16 rows][4 blocks][4 kg] fp16     H*W/16 bytes
+// MODE 0: gate/up (A = gathered x); MODE 1: down (A = h fp32 rounded to bf16).
+constexpr uint32_t kMinus136x2 = 0xC308C308u;  // bf16 -136 in both halves
+
+template <int MODE, bool XF32, int TG>
+__global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void* __restrict__ a_src,
+                                                          const int32_t* __restrict__ row_tok,
+                                                          float* __restrict__ out, int hstride,
+                                                          int nblk) {
+  constexpr bool AF32 = MODE == 1 ? true : XF32;
+  constexpr bool SPLIT = MODE == 0 && XF32;   // down rounds h to bf16 (one MFMA per block)
   const int tile = blockIdx.x / nblk, nb = blockIdx.x % nblk;
   TileInfo ti;
   if (!tile_info(g, tile, ti)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = nb * 64 + wave * 16;
-  const int H = g.H;
-  if (n0 >= H) return;
-  const int K = ti.width, nk = K / 32;
-  const uint8_t* wp = g.packed + (size_t)ti.group * g.expert_bytes +
-                      (size_t)2 * ti.width * H * 2 + (size_t)(n0 / 16) * nk * kFragBytes +
-                      lane * 16;
-
-  size_t hoff[TG];
-  bool ok[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    const int r = t * 16 + (lane & 15);
-    ok[t] = r < ti.nrows;
-    hoff[t] = (size_t)(ti.row0 + (ok[t] ? r : 0)) * hstride + (lane >> 4) * 8;
+  const int H = g.H, W = ti.width;
+  const uint8_t* base = g.packed + (size_t)ti.group * g.expert_bytes;
+  int f0, K;
+  const uint8_t *qp, *sp;
+  TileRows<TG> rows;
+  if (MODE == 0) {
+    f0 = nb * 128 + wave * 32;
+    if (f0 >= W) return;
+    K = H;
+    qp = base + (size_t)(f0 / 32) * (K / 128) * kBlockBytes;
+    sp = base + (size_t)W * H + (size_t)(f0 / 32) * (K / 128) * 512;
+    rows.gather(ti, row_tok, g.T, H, lane);
+  } else {
+    f0 = nb * 256 + wave * 64;
+    if (f0 >= H) return;
+    K = W;
+    const uint8_t* dbase = base + (size_t)W * H + (size_t)W * H / 8;
+    qp = dbase + (size_t)(f0 / 64) * (K / 128) * kBlockBytes;
+    sp = dbase + (size_t)H * W / 2 + (size_t)(f0 / 64) * (K / 128) * 512;
+    rows.direct(ti, hstride, lane);
   }
-  f32x4 acc[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  qp += lane * 16;
+  sp += (lane & 15) * 32;
+  const int nkb = K / 128;
+  const bf16x8 m136 = as_bf16x8(u32x4{kMinus136x2, kMinus136x2, kMinus136x2, kMinus136x2});
 
-  u32x4 wa[U], wn[U];
+  f32x4 acc[TG][4];
 #pragma unroll
-  for (int u = 0; u < U; ++u) wa[u] = load16_stream(wp + (size_t)u * kFragBytes);
-  for (int k0 = 0; k0 < nk; k0 += U) {
-    BRow<true> b[U][TG];
+  for (int t = 0; t < TG; ++t)
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < TG; ++t) b[u][t].load(h, hoff[t] + (size_t)(k0 + u) * 32, ok[t]);
-    const bool more = k0 + U < nk;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (more) wn[u] = load16_stream(wp + (size_t)(k0 + U + u) * kFragBytes);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < TG; ++t) {
-        bf16x8 bh, bl;
-        b[u][t].operands(bh, bl);
-        acc[t] = mma<true>(as_bf16x8(wa[u]), bh, bl, acc[t]);
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u) wa[u] = wn[u];
-  }
+    for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  u32x4 q[4], qn[4], s[2], sn[2];
+  ARow<AF32> a[4][TG], an[4][TG];
 #pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    if (!ok[t]) continue;
-    const size_t row = (size_t)ti.row0 + t * 16 + (lane & 15);
-    float* yp = y + row * H + n0 + (lane >> 4) * 4;
-    *reinterpret_cast<f32x4*>(yp) = acc[t];
-  }
-}
-
-// ------------------------------------------------------------------ INT4 helpers
-// Packed INT4 region of one group of width W (rows of gate/up = W, of down = H):
-//   gate/up q      [W/16][H/128][2][64][16 B]          W*H bytes
-//   gate/up scales [W/16][H/128][2][4 quads][4 kg][4]  W*H/8 bytes (fp16)
-//   down q         [H/16][W/128][64][16 B]              H*W/2 bytes
-//   down scales    [H/16][W/128][4][4][4]               H*W/16 bytes
-__device__ __forceinline__ void load_scales(const uint8_t* p, float s[4][4]) {
-  const u32x4 a = load16_stream(p), b = load16_stream(p + 16);
-  const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  for (int j = 0; j < 4; ++j) q[j] = load16_stream(qp + j * kFragBytes);
+  s[0] = load16_stream(sp);
+  s[1] = load16_stream(sp + 16);
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t word = w[(kg * 4 + i) >> 1];
-      const uint16_t bits = (uint16_t)(((kg * 4 + i) & 1) ? (word >> 16) : (word & 0xffff));
-      s[kg][i] = (float)__builtin_bit_cast(_Float16, bits);
-    }
-}
+    for (int t = 0; t < TG; ++t) a[kg][t].load(a_src, rows.off[t] + kg * 32, rows.ok[t]);
 
-constexpr uint32_t kMinus136x2 = 0xC308C308u;  // bf16 -136 in both halves
-
-template <bool F32, int TG>
-__device__ __forceinline__ void int4_group_step(const u32x4& qa, const float (&sc)[4][4],
-                                                const BRow<F32> (&b)[4][TG], f32x4 (&acc)[TG],
-                                                int kg) {
-  const bf16x8 m136 = as_bf16x8(u32x4{kMinus136x2, kMinus136x2, kMinus136x2, kMinus136x2});
-  const bf16x8 a = int4_to_bf16x8_biased(qa[kg]);
-#pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    bf16x8 bh, bl;
-    b[kg][t].operands(bh, bl);
-    f32x4 p = mma<F32>(m136, bh, bl, f32x4{0.f, 0.f, 0.f, 0.f});
-    p = mma<F32>(a, bh, bl, p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] += sc[kg][i] * p[i];
-  }
-}
-
-// ------------------------------------------------------------------ INT4 gate/up
-template <bool F32, int TG>
-__global__ __launch_bounds__(256) void gateup_int4_kernel(GemmGeom g, const void* __restrict__ x,
-                                                          const int32_t* __restrict__ row_tok,
-                                                          int T, float* __restrict__ hout,
-                                                          int hstride, int nblk) {
-  const int tile = blockIdx.x / nblk, nb = blockIdx.x % nblk;
-  TileInfo ti;
-  if (!tile_info(g, tile, ti)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int f0 = nb * 64 + wave * 16;
-  if (f0 >= ti.width) return;
-  const int H = g.H, nkb = H / 128;
-  const uint8_t* base = g.packed + (size_t)ti.group * g.expert_bytes;
-  const uint8_t* qp = base + (size_t)(f0 / 16) * nkb * 2 * kFragBytes + lane * 16;
-  const uint8_t* sp = base + (size_t)ti.width * H + (size_t)(f0 / 16) * nkb * 2 * 128 +
-                      (lane >> 4) * 32;
-
-  size_t xoff[TG];
-  bool ok[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    const int r = t * 16 + (lane & 15);
-    ok[t] = r < ti.nrows;
-    int tok = ok[t] ? row_tok[ti.row0 + r] : 0;
-    tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
-    xoff[t] = (size_t)tok * H + (lane >> 4) * 8;
-  }
-  f32x4 accg[TG], accu[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) accg[t] = accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 qg = load16_stream(qp), qu = load16_stream(qp + kFragBytes);
-  float sg[4][4], su[4][4];
-  load_scales(sp, sg);
-  load_scales(sp + 128, su);
   for (int kb = 0; kb < nkb; ++kb) {
-    BRow<F32> b[4][TG];
+    const bool more = kb + 1 < nkb;
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        qn[j] = load16_stream(qp + (size_t)(kb + 1) * kBlockBytes + j * kFragBytes);
+      sn[0] = load16_stream(sp + (size_t)(kb + 1) * 512);
+      sn[1] = load16_stream(sp + (size_t)(kb + 1) * 512 + 16);
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+        for (int t = 0; t < TG; ++t)
+          an[kg][t].load(a_src, rows.off[t] + (size_t)(kb + 1) * 128 + kg * 32, rows.ok[t]);
+    }
+    // scales of this lane's weight row: [4 blocks][4 kg] fp16
+    float sc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        const int e = j * 4 + kg;
+        const uint32_t word = s[e >> 3][(e >> 1) & 3];
+        const uint16_t bits = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+        sc[j][kg] = (float)__builtin_bit_cast(_Float16, bits);
+      }
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
-      for (int t = 0; t < TG; ++t) b[kg][t].load(x, xoff[t] + (size_t)kb * 128 + kg * 32, ok[t]);
-    u32x4 ng = qg, nu = qu;
-    float nsg[4][4], nsu[4][4];
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      ng = load16_stream(qp + (size_t)(kb + 1) * 2 * kFragBytes);
-      nu = load16_stream(qp + (size_t)(kb + 1) * 2 * kFragBytes + kFragBytes);
-      load_scales(sp + (size_t)(kb + 1) * 256, nsg);
-      load_scales(sp + (size_t)(kb + 1) * 256 + 128, nsu);
-    }
+      for (int t = 0; t < TG; ++t) {
+        bf16x8 ah, al;
+        a[kg][t].operands(ah, al);
+        const f32x4 corr = mma<SPLIT>(ah, al, m136, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-      int4_group_step<F32, TG>(qg, sg, b, accg, kg);
-      int4_group_step<F32, TG>(qu, su, b, accu, kg);
-    }
-    if (more) {
-      qg = ng;
-      qu = nu;
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 p = mma<SPLIT>(ah, al, int4_to_bf16x8_biased(q[j][kg]), corr);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sg[a][i] = nsg[a][i];
-          su[a][i] = nsu[a][i];
+          for (int i = 0; i < 4; ++i) acc[t][j][i] += sc[j][kg] * p[i];
         }
+      }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[j] = qn[j];
+      s[0] = sn[0];
+      s[1] = sn[1];
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+        for (int t = 0; t < TG; ++t) a[kg][t] = an[kg][t];
     }
   }
 
 #pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    if (!ok[t]) continue;
-    const size_t row = (size_t)ti.row0 + t * 16 + (lane & 15);
-    const int f = f0 + (lane >> 4) * 4;
-    f32x4 hv;
+  for (int t = 0; t < TG; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hv[i] = silu(accg[t][i]) * accu[t][i];
-    *reinterpret_cast<f32x4*>(hout + row * hstride + f) = hv;
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int r = t * 16 + (lane >> 4) * 4 + i;
+      if (r >= ti.nrows) continue;
+      const size_t row = (size_t)ti.row0 + r;
+      if (MODE == 0) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          out[row * hstride + f0 + f * 16 + (lane & 15)] = silu(acc[t][f][i]) * acc[t][2 + f][i];
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) out[row * H + f0 + f * 16 + (lane & 15)] = acc[t][f][i];
+      }
+    }
 }
 
-// ------------------------------------------------------------------ INT4 down
-template <int TG>
-__global__ __launch_bounds__(256) void down_int4_kernel(GemmGeom g, const float* __restrict__ h,
-                                                        int hstride, float* __restrict__ y,
-                                                        int nblk) {
-  const int tile = blockIdx.x / nblk, nb = blockIdx.x % nblk;
-  TileInfo ti;
-  if (!tile_info(g, tile, ti)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = nb * 64 + wave * 16;
-  const int H = g.H;
-  if (n0 >= H) return;
-  const int W = ti.width, nkb = W / 128;
-  const uint8_t* base = g.packed + (size_t)ti.group * g.expert_bytes + (size_t)W * H +
-                        (size_t)W * H / 8;
-  const uint8_t* qp = base + (size_t)(n0 / 16) * nkb * kFragBytes + lane * 16;
-  const uint8_t* sp = base + (size_t)H * W / 2 + (size_t)(n0 / 16) * nkb * 128 + (lane >> 4) * 32;
-
-  size_t hoff[TG];
-  bool ok[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    const int r = t * 16 + (lane & 15);
-    ok[t] = r < ti.nrows;
-    hoff[t] = (size_t)(ti.row0 + (ok[t] ? r : 0)) * hstride + (lane >> 4) * 8;
-  }
-  f32x4 acc[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 q = load16_stream(qp);
-  float s[4][4];
-  load_scales(sp, s);
-  for (int kb = 0; kb < nkb; ++kb) {
-    BRow<true> b[4][TG];
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-      for (int t = 0; t < TG; ++t) b[kg][t].load(h, hoff[t] + (size_t)kb * 128 + kg * 32, ok[t]);
-    u32x4 nq = q;
-    float ns[4][4];
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      nq = load16_stream(qp + (size_t)(kb + 1) * kFragBytes);
-      load_scales(sp + (size_t)(kb + 1) * 128, ns);
-    }
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) int4_group_step<true, TG>(q, s, b, acc, kg);
-    if (more) {
-      q = nq;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[a][i] = ns[a][i];
-    }
-  }
-
-#pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    if (!ok[t]) continue;
-    const size_t row = (size_t)ti.row0 + t * 16 + (lane & 15);
-    float* yp = y + row * H + n0 + (lane >> 4) * 4;
-    *reinterpret_cast<f32x4*>(yp) = acc[t];
-  }
-}
-
-template <int TG>
-hipError_t gateup_tg(const GemmGeom& g, bool int4, bool f32, const void* x,
-                     const int32_t* row_tok, int T, float* h, int hstride, hipStream_t s) {
+template <int MODE, int TG>
+hipError_t launch_mode(const GemmGeom& g, bool int4, bool f32, const void* a,
+                       const int32_t* row_tok, float* out, int hstride, hipStream_t s) {
   const int wmax = g.I > g.Is ? g.I : g.Is;
-  const int nblk = (wmax + 63) / 64;
+  const int nblk = MODE == 0 ? (wmax + 127) / 128 : (g.H + 255) / 256;
   dim3 grid((unsigned)g.max_tiles * nblk), block(256);
-  const int nk = g.H / 32;
+#define MOE_L(KERNEL) \
+  hipLaunchKernelGGL(KERNEL, grid, block, 0, s, g, a, row_tok, out, hstride, nblk)
   if (int4) {
-    if (f32)
-      hipLaunchKernelGGL((gateup_int4_kernel<true, TG>), grid, block, 0, s, g, x, row_tok, T, h,
-                         hstride, nblk);
-    else
-      hipLaunchKernelGGL((gateup_int4_kernel<false, TG>), grid, block, 0, s, g, x, row_tok, T, h,
-                         hstride, nblk);
-  } else if (nk % 4 == 0) {
-    if (f32)
-      hipLaunchKernelGGL((gateup_bf16_kernel<true, TG, 4>), grid, block, 0, s, g, x, row_tok, T,
-                         h, hstride, nblk);
-    else
-      hipLaunchKernelGGL((gateup_bf16_kernel<false, TG, 4>), grid, block, 0, s, g, x, row_tok, T,
-                         h, hstride, nblk);
+    if (f32) MOE_L((stream_int4_kernel<MODE, true, TG>));
+    else MOE_L((stream_int4_kernel<MODE, false, TG>));
   } else {
-    if (f32)
-      hipLaunchKernelGGL((gateup_bf16_kernel<true, TG, 2>), grid, block, 0, s, g, x, row_tok, T,
-                         h, hstride, nblk);
-    else
-      hipLaunchKernelGGL((gateup_bf16_kernel<false, TG, 2>), grid, block, 0, s, g, x, row_tok, T,
-                         h, hstride, nblk);
+    // k-steps per group: 2 when every group's K/32 is even (H % 64 == 0 always;
+    // the expert widths are only multiples of 32)
+    const bool even = MODE == 0 || ((g.I / 32) % 2 == 0 && (g.Is / 32) % 2 == 0);
+    if (even) {
+      if (f32) MOE_L((stream_bf16_kernel<MODE, true, TG, 2>));
+      else MOE_L((stream_bf16_kernel<MODE, false, TG, 2>));
+    } else {
+      if (f32) MOE_L((stream_bf16_kernel<MODE, true, TG, 1>));
+      else MOE_L((stream_bf16_kernel<MODE, false, TG, 1>));
+    }
   }
+#undef MOE_L
   return hipGetLastError();
 }
 
-template <int TG>
-hipError_t down_tg(const GemmGeom& g, bool int4, const float* h, int hstride, float* y,
-                   hipStream_t s) {
-  const int nblk = g.H / 64;
-  dim3 grid((unsigned)g.max_tiles * nblk), block(256);
-  const int nk_i = g.I / 32, nk_s = g.Is > 0 ? g.Is / 32 : nk_i;
-  const bool u4 = nk_i % 4 == 0 && nk_s % 4 == 0;
-  if (int4)
-    hipLaunchKernelGGL((down_int4_kernel<TG>), grid, block, 0, s, g, h, hstride, y, nblk);
-  else if (u4)
-    hipLaunchKernelGGL((down_bf16_kernel<TG, 4>), grid, block, 0, s, g, h, hstride, y, nblk);
-  else
-    hipLaunchKernelGGL((down_bf16_kernel<TG, 1>), grid, block, 0, s, g, h, hstride, y, nblk);
-  return hipGetLastError();
+template <int MODE>
+hipError_t launch_tg(const GemmGeom& g, bool int4, bool f32, const void* a,
+                     const int32_t* row_tok, float* out, int hstride, hipStream_t s) {
+  switch (g.tg) {
+    case 1: return launch_mode<MODE, 1>(g, int4, f32, a, row_tok, out, hstride, s);
+    case 2: return launch_mode<MODE, 2>(g, int4, f32, a, row_tok, out, hstride, s);
+    default: return launch_mode<MODE, 4>(g, int4, f32, a, row_tok, out, hstride, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gateup(const GemmGeom& g, bool int4, bool act_f32, const void* x,
                          const int32_t* row_tok, float* h, int hstride, hipStream_t s) {
-  const int T = g.T;
-  switch (g.tg) {
-    case 1: return gateup_tg<1>(g, int4, act_f32, x, row_tok, T, h, hstride, s);
-    case 2: return gateup_tg<2>(g, int4, act_f32, x, row_tok, T, h, hstride, s);
-    default: return gateup_tg<4>(g, int4, act_f32, x, row_tok, T, h, hstride, s);
-  }
+  return launch_tg<0>(g, int4, act_f32, x, row_tok, h, hstride, s);
 }
 
 hipError_t launch_down(const GemmGeom& g, bool int4, const float* h, int hstride, float* y,
                        hipStream_t s) {
-  switch (g.tg) {
-    case 1: return down_tg<1>(g, int4, h, hstride, y, s);
-    case 2: return down_tg<2>(g, int4, h, hstride, y, s);
-    default: return down_tg<4>(g, int4, h, hstride, y, s);
-  }
+  return launch_tg<1>(g, int4, true, h, nullptr, y, hstride, s);
 }
 
 }  // namespace moe

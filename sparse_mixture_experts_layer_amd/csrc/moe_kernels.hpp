@@ -45,13 +45,13 @@ hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* in
                           int k, int P, int has_shared, void* out, int T, hipStream_t s);
 
 // ---- weight packing ----------------------------------------------------------
-// bf16 [N][K] (G sources interleaved per 16-row block) -> fragments.
-hipError_t launch_pack_bf16(const uint16_t* src0, const uint16_t* src1, int G, int N, int K,
-                            int batch, size_t src_batch_stride, uint8_t* dst,
+// bf16 [N][K] of S sources (1 or 2) -> blocks of F*S fragments per 32-k step.
+hipError_t launch_pack_bf16(const uint16_t* src0, const uint16_t* src1, int S, int F, int N,
+                            int K, int batch, size_t src_batch_stride, uint8_t* dst,
                             size_t dst_batch_stride, hipStream_t s);
-// INT4 nibbles [N][K/2] + fp16 scales [N][K/32] -> 16x128 blocks + scale quads.
+// INT4 nibbles [N][K/2] + fp16 scales [N][K/32] -> blocks per 128-k step + scales.
 hipError_t launch_pack_int4(const uint8_t* q0, const uint8_t* q1, const uint16_t* s0,
-                            const uint16_t* s1, int G, int N, int K, int batch,
+                            const uint16_t* s1, int S, int F, int N, int K, int batch,
                             size_t q_batch_stride, size_t s_batch_stride, uint8_t* dst_q,
                             uint8_t* dst_s, size_t dst_batch_stride, hipStream_t s);
 
