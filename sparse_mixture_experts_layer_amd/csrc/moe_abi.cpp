@@ -90,8 +90,8 @@ moe_status_t check_config(const moe_layer_config_t* c) {
 
 // Per-call plan and workspace layout.
 struct Plan {
-  int T, P, ks, tg, max_tiles, has_shared, hstride;
-  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, h, y, total;
+  int T, P, ks, tg, max_tiles, has_shared, hstride, tiled;
+  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, h, h_lo, y, total;
 };
 
 Plan make_plan(const moe_layer& L, int T) {
@@ -100,9 +100,10 @@ Plan make_plan(const moe_layer& L, int T) {
   p.T = T;
   p.P = T * c.top_k;
   p.has_shared = c.shared_inter > 0;
-  // router: split H so that small batches still spread over the CUs
-  const int ne = c.num_experts <= 16 ? 1 : (c.num_experts <= 32 ? 2 : 6);
-  const int wgs = ((T + 63) / 64) * ((c.num_experts + 16 * ne - 1) / (16 * ne));
+  // router: split H so that small batches still spread over the CUs (the
+  // grid mirrors launch_router_logits: 16*nt tokens x 64*ne experts per block)
+  const int nt = T <= 32 ? 2 : 4, ne = T <= 256 ? 1 : 2;
+  const int wgs = ((T + 16 * nt - 1) / (16 * nt)) * ((c.num_experts + 64 * ne - 1) / (64 * ne));
   p.ks = 1;
   while (wgs * p.ks < 256 && p.ks < 8 && (c.hidden / 32) % (2 * p.ks) == 0) p.ks *= 2;
   // expert GEMM tile rows: 16 when experts see about one row (decode), 32 or
@@ -110,6 +111,10 @@ Plan make_plan(const moe_layer& L, int T) {
   const double rows_per_expert = (double)p.P / c.num_experts;
   p.tg = rows_per_expert < 2.0 ? 1 : (rows_per_expert < 24.0 ? 2 : 4);
   if (c.weight_dtype == MOE_INT4_G32 && p.tg > 2) p.tg = 2;  // register budget
+  // MFMA-bound regime: LDS-staged 128-row tiles with bf16 h (bf16 weights and
+  // activations only)
+  p.tiled = rows_per_expert >= 64.0 && c.weight_dtype == MOE_BF16 && c.act_dtype == MOE_BF16;
+  if (p.tiled) p.tg = 8;
   const int bm = 16 * p.tg;
   const int nz = c.num_experts < p.P ? c.num_experts : p.P;
   p.max_tiles = nz + p.P / bm + (p.has_shared ? (T + bm - 1) / bm : 0) + 1;
@@ -135,6 +140,7 @@ Plan make_plan(const moe_layer& L, int T) {
   p.tiles = take((size_t)p.max_tiles * 4);
   p.ntiles = take(4);
   p.h = take((size_t)rows * p.hstride * 4);
+  p.h_lo = take(p.tiled && p.has_shared ? (size_t)T * p.hstride * 2 : 0);
   p.y = take((size_t)rows * c.hidden * 4);
   p.total = o;
   return p;
@@ -344,9 +350,19 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g.counts = counts;
   g.max_tiles = p.max_tiles;
   g.tg = p.tg;
-  if (e == hipSuccess) e = moe::launch_gateup(g, int4, f32, x, row_tok, h, p.hstride, stream);
-  if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = moe::launch_down(g, int4, h, p.hstride, y, stream);
+  if (p.tiled) {
+    uint16_t* hb = reinterpret_cast<uint16_t*>(h);
+    uint16_t* hl = reinterpret_cast<uint16_t*>(ws + p.h_lo);
+    if (e == hipSuccess)
+      e = moe::launch_gateup_tiled(g, static_cast<const uint16_t*>(x), row_tok, hb, hl,
+                                   p.hstride, stream);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = moe::launch_down_tiled(g, hb, hl, p.hstride, y, stream);
+  } else {
+    if (e == hipSuccess) e = moe::launch_gateup(g, int4, f32, x, row_tok, h, p.hstride, stream);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = moe::launch_down(g, int4, h, p.hstride, y, stream);
+  }
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
     e = moe::launch_combine(f32, y, H, inv, wts, k, p.P, p.has_shared, out, T, stream);

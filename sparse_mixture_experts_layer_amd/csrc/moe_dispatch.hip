@@ -25,22 +25,32 @@ namespace {
 constexpr int kDispWaves = 16;
 constexpr int kDispThreads = kDispWaves * kWave;
 
-// Exclusive scan of buf[0..n) in place (n <= kDispThreads); returns the total.
-__device__ int block_exclusive_scan(int* buf, int* tmp, int n) {
+// Exclusive scan of buf[0..n) in place by wave 0 (n <= 64 * 16); every thread
+// gets the total.  Lane l owns a run of ceil(n/64) consecutive entries.
+__device__ int block_exclusive_scan(int* buf, int* total_slot, int n) {
   const int tid = threadIdx.x;
-  int v = tid < n ? buf[tid] : 0;
-  tmp[tid] = v;
   __syncthreads();
-  for (int off = 1; off < kDispThreads; off <<= 1) {
-    int add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  if (tid < kWave) {
+    const int per = (n + kWave - 1) / kWave;
+    const int beg = min(n, tid * per), end = min(n, beg + per);
+    int sum = 0;
+    for (int i = beg; i < end; ++i) sum += buf[i];
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (tid >= d) incl += o;
+    }
+    int run = incl - sum;
+    for (int i = beg; i < end; ++i) {
+      const int v = buf[i];
+      buf[i] = run;
+      run += v;
+    }
+    if (tid == kWave - 1) *total_slot = incl;
   }
-  const int total = tmp[kDispThreads - 1];
-  if (tid < n) buf[tid] = tmp[tid] - v;
   __syncthreads();
-  return total;
+  return *total_slot;
 }
 
 __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
@@ -53,16 +63,16 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   __shared__ int tot[kMaxExperts + 1];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int ntile[kMaxExperts + 1];
-  __shared__ int scan_tmp[kDispThreads];
+  __shared__ int scan_total;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int P = T * k;
   const int tw = (T + kDispWaves - 1) / kDispWaves;  // tokens per wave
   const int tbeg = min(T, wave * tw), tend = min(T, tbeg + tw);
 
-  for (int i = tid; i < kDispWaves * kMaxExperts; i += kDispThreads) {
-    (&hist[0][0])[i] = 0;
-    (&mask[0][0])[i] = 0ull;
+  for (int i = tid; i < kDispWaves * E; i += kDispThreads) {
+    hist[i / E][i % E] = 0;
+    mask[i / E][i % E] = 0ull;
   }
   __syncthreads();
 
@@ -88,7 +98,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     off[tid] = run;
   }
   __syncthreads();
-  block_exclusive_scan(off, scan_tmp, E);
+  block_exclusive_scan(off, &scan_total, E);
   if (tid < E) {
     counts[tid] = tot[tid];
     offsets[tid] = off[tid];
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   __syncthreads();
 
   // tile list: groups in order 0..E, m-tiles in order inside a group
-  const int total_tiles = block_exclusive_scan(ntile, scan_tmp, E + 1);
+  const int total_tiles = block_exclusive_scan(ntile, &scan_total, E + 1);
   // ntile[] now holds each group's first tile; the tile count is recomputed.
   if (tid <= E) {
     const int c = tid < E ? tot[tid] : (has_shared ? T : 0);

@@ -1,0 +1,217 @@
+// Grouped expert GEMMs for large batches (prefill): LDS-staged 128 x 256 tiles
+// on bf16 MFMA, the MFMA-bound regime where each expert sees hundreds of rows.
+//   gate/up:  h[r][f] = bf16(silu(x_r . Wg[f]) * (x_r . Wu[f]))   (r gathered via row_tok)
+//   down:     Y[r][n] = h_r . Wd[n]                                (fp32)
+// Expert FFN shape: llm-atlas "Step-3.5-Flash", "Champs bruts du config.json"
+// (moe_intermediate_size, share_expert_dim, hidden_size); SiLU gating is the
+// reading taken for the swiglu fields.
+//
+// Workgroup: 4 waves, tile = 128 rows x 256 weight rows; wave (wm, wn) owns
+// rows 64*wm .. +63 and weight rows 128*wn .. +127 (4 x 8 fragments of
+// 16x16, 128 fp32 accumulators per lane).  K advances 32 per stage through a
+// 3-stage LDS ring (24 KiB per stage): each stage is 8 A fragments (token
+// rows, gathered straight from x by per-lane addresses) and 16 B fragments
+// (packed weights), each 1 KiB and each written by one wave-wide
+// global->LDS load in MFMA operand order, so every LDS read is a contiguous
+// 1 KiB ds_read_b128 with no bank conflicts and no register staging.
+// Two stages are in flight while the third is multiplied.
+//
+// Precision: routed rows keep h in bf16 (one rounding, what the MFMA takes).
+// The shared expert enters the output unweighted, so its rounding error would
+// be the largest term of the output error: its h is stored as bf16 hi + lo
+// (a second plane) and its down GEMM runs a second pass over lo.
+//
+// Tile order: the work list (tile-major, weight blocks fastest) is cut into 8
+// contiguous chunks, one per XCD (workgroups are dealt round-robin over the
+// XCDs), so the m-tiles of one expert run side by side on one XCD and share
+// its L2: an expert's weights are read from HBM about once per N-block
+// instead of once per m-tile.
+#include "moe_common.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kTM = 128;                      // rows per tile
+constexpr int kTN = 256;                      // weight rows per tile
+constexpr int kStages = 3;
+constexpr int kAFrags = kTM / 16;             // 8
+constexpr int kBFrags = kTN / 16;             // 16
+constexpr int kStageBytes = (kAFrags + kBFrags) * kFragBytes;  // 24 KiB
+constexpr int kXcds = 8;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// One wave-wide 16-byte-per-lane load into LDS at `lds` (+ 16 * lane).
+__device__ __forceinline__ void load_frag(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)lds, 16, 0, 0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_t* __restrict__ a_src,
+                                                    const int32_t* __restrict__ row_tok,
+                                                    void* __restrict__ out, int hstride,
+                                                    uint16_t* __restrict__ h_lo, int nblk) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
+
+  // XCD-contiguous work order
+  const int total = *g.ntiles * nblk;
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= chunk) return;
+  const int w = (blockIdx.x % kXcds) * chunk + slot;
+  if (w >= total) return;
+  const int tile = w / nblk, nb = w % nblk;
+  const int v = g.tiles[tile];
+  const int group = tile_group(v);
+  const int row0 = g.offsets[group] + tile_m(v) * kTM;
+  const int nrows = min(kTM, g.counts[group] - tile_m(v) * kTM);
+  if (nrows <= 0) return;
+  const int width = group == g.E ? g.Is : g.I;
+  const int H = g.H;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = MODE == 0 ? H : width;
+  const int nk = K / 32;
+  // weight blocks of 64 rows (gate/up: 32 features x {gate, up}; down: 64 outputs)
+  const int nblocks = MODE == 0 ? width / 32 : H / 64;
+
+  // this wave's two A fragments (rows 16*(2*wave) .. +31 of the tile); for the
+  // shared group's down GEMM, pass 1 reads the lo plane (row - shared_base)
+  const bool shared = group == g.E;
+  const int shared_base = g.offsets[g.E];
+  const int npass = (MODE == 1 && shared) ? 2 : 1;
+  size_t a_off[2];
+  auto set_rows = [&](int pass) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      int r = (2 * wave + f) * 16 + (lane & 15);
+      if (r >= nrows) r = 0;  // any valid row: its C row is never stored
+      if (MODE == 0) {
+        int tok = row_tok[row0 + r];
+        tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
+        a_off[f] = (size_t)tok * H + (lane >> 4) * 8;
+      } else {
+        const int row = pass == 0 ? row0 + r : row0 + r - shared_base;
+        a_off[f] = (size_t)row * hstride + (lane >> 4) * 8;
+      }
+    }
+  };
+  // this wave's B block (4 fragments, 4 KiB per k-step)
+  const int bblk = nb * 4 + wave;
+  const bool b_ok = bblk < nblocks;
+  const uint8_t* bsrc = g.packed + (size_t)group * g.expert_bytes +
+                        (MODE == 0 ? 0 : (size_t)2 * width * H * 2) +
+                        (size_t)(b_ok ? bblk : 0) * nk * 4 * kFragBytes + lane * 16;
+
+  const uint16_t* a_base = a_src;
+  auto issue = [&](int kk, int stage) {
+    uint8_t* st = lds + stage * kStageBytes;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      load_frag(a_base + a_off[f] + (size_t)kk * 32, st + (2 * wave + f) * kFragBytes);
+    if (b_ok) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        load_frag(bsrc + (size_t)kk * 4 * kFragBytes + q * kFragBytes,
+                  st + (kAFrags + 4 * wave + q) * kFragBytes);
+    }
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int pass = 0; pass < npass; ++pass) {
+    set_rows(pass);
+    a_base = pass == 0 ? a_src : h_lo;
+    if (pass > 0) asm volatile("s_barrier" ::: "memory");  // ring free before refilling
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    for (int kk = 0; kk < nk; ++kk) {
+      // stage kk must have landed; stage kk+1 (if issued) may still be in flight
+      // (a plain s_barrier: __syncthreads' release fence would drain every
+      // outstanding LDS load, including the stage prefetched for the next step)
+      if (kk + 1 < nk) {
+        if (b_ok) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (kk + 2 < nk) issue(kk + 2, (kk + 2) % kStages);
+      const uint8_t* st = lds + (kk % kStages) * kStageBytes;
+      bf16x8 a[4], b[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        a[m] = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(st + (wm * 4 + m) * kFragBytes + lane * 16));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + (kAFrags + wn * 8 + j) * kFragBytes +
+                                                          lane * 16));
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
+    }
+  }
+
+  // epilogue: lane holds rows 4*(lane/16)+i of each 16-row fragment, column lane%16
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 64 + m * 16 + (lane >> 4) * 4 + i;
+      if (r >= nrows) continue;
+      const size_t row = (size_t)row0 + r;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const int blk = nb * 4 + wn * 2 + jb;
+        if (blk >= nblocks) continue;
+        if (MODE == 0) {
+          uint16_t* hp = reinterpret_cast<uint16_t*>(out) + row * hstride + blk * 32 + (lane & 15);
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const float hv = silu(acc[m][jb * 4 + f][i]) * acc[m][jb * 4 + 2 + f][i];
+            const uint16_t hi = f32_to_bf16_bits(hv);
+            hp[f * 16] = hi;
+            if (shared)
+              h_lo[(row - shared_base) * hstride + blk * 32 + f * 16 + (lane & 15)] =
+                  f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
+          }
+        } else {
+          float* yp = reinterpret_cast<float*>(out) + row * H + blk * 64 + (lane & 15);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) yp[f * 16] = acc[m][jb * 4 + f][i];
+        }
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32_t* row_tok,
+                               uint16_t* h, uint16_t* h_lo, int hstride, hipStream_t s) {
+  const int wmax = g.I > g.Is ? g.I : g.Is;
+  const int nblk = (2 * wmax + kTN - 1) / kTN;
+  const size_t items = (size_t)g.max_tiles * nblk;
+  dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(256);
+  hipLaunchKernelGGL((tiled_kernel<0>), grid, block, 0, s, g, x, row_tok, h, hstride, h_lo, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_t* h_lo,
+                             int hstride, float* y, hipStream_t s) {
+  const int nblk = (g.H + kTN - 1) / kTN;
+  const size_t items = (size_t)g.max_tiles * nblk;
+  dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(256);
+  hipLaunchKernelGGL((tiled_kernel<1>), grid, block, 0, s, g, h, nullptr, y, hstride,
+                     const_cast<uint16_t*>(h_lo), nblk);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -40,6 +40,13 @@ hipError_t launch_gateup(const GemmGeom& g, bool int4, bool act_f32, const void*
 hipError_t launch_down(const GemmGeom& g, bool int4, const float* h, int hstride, float* y,
                        hipStream_t s);
 
+// Large-batch (MFMA-bound) variants: 128-row tiles (g.tg must be 8), bf16 h;
+// the shared group's h also gets a bf16 remainder plane h_lo ([T][hstride]).
+hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32_t* row_tok,
+                               uint16_t* h, uint16_t* h_lo, int hstride, hipStream_t s);
+hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_t* h_lo,
+                             int hstride, float* y, hipStream_t s);
+
 // ---- combine: out[t] = Y[shared row of t] + sum_j w[t,j] Y[inv[t,j]] -------
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
                           int k, int P, int has_shared, void* out, int T, hipStream_t s);

@@ -18,27 +18,29 @@
 namespace moe {
 namespace {
 
-// One workgroup: 64 tokens (16 per wave) x (16 * NE) experts x one K slice.
-// Experts are on the MFMA A side, tokens on the B side, so each lane ends with
-// 4 consecutive experts of one token.
-template <bool XF32, int NE>
+// One workgroup = 4 waves; a wave computes 16*NT tokens x 16*NE experts over
+// one K slice.  Tokens are the MFMA A operand and router rows the B operand,
+// so a lane ends with one expert column of 4 token rows per tile.
+template <bool XF32, int NT, int NE>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv,
                                                             const uint16_t* __restrict__ wr,
                                                             float* __restrict__ part, int T, int H,
                                                             int E, int kchunk) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * 64 + wave * 16;
-  if (t0 >= T) return;
-  const int e0 = blockIdx.y * (16 * NE);
+  const int t0 = blockIdx.x * 16 * NT;
+  const int e0 = (blockIdx.y * 4 + wave) * 16 * NE;
+  if (e0 >= E) return;
   const int kbeg = blockIdx.z * kchunk;
-  const int tok = t0 + (lane & 15);
-  const bool tok_ok = tok < T;
   const int kl = (lane >> 4) * 8;
 
-  f32x4 acc[NE];
+  size_t xoff[NT];
+  bool xok[NT];
 #pragma unroll
-  for (int n = 0; n < NE; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  for (int t = 0; t < NT; ++t) {
+    const int tok = t0 + t * 16 + (lane & 15);
+    xok[t] = tok < T;
+    xoff[t] = (size_t)(xok[t] ? tok : 0) * H + kl;
+  }
   const uint16_t* wrow[NE];
   bool wok[NE];
 #pragma unroll
@@ -47,65 +49,79 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
     wok[n] = e < E;
     wrow[n] = wr + (size_t)(wok[n] ? e : 0) * H + kl;
   }
+  f32x4 acc[NT][NE];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int n = 0; n < NE; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int k = kbeg; k < kbeg + kchunk; k += 32) {
-    u32x4 bh = {0, 0, 0, 0}, bl = {0, 0, 0, 0};
-    if (XF32) {
-      const float* xp = reinterpret_cast<const float*>(xv) + (size_t)tok * H + k + kl;
-      if (tok_ok) {
-        float v[8];
-        u32x4 a0 = load16(xp), a1 = load16(xp + 4);
+    u32x4 b[NE];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = __uint_as_float(a0[i]);
-          v[4 + i] = __uint_as_float(a1[i]);
+    for (int n = 0; n < NE; ++n) b[n] = wok[n] ? load16(wrow[n] + k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      u32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
+      if (XF32) {
+        if (xok[t]) {
+          const float* xp = reinterpret_cast<const float*>(xv) + xoff[t] + k;
+          const u32x4 a0 = load16(xp), a1 = load16(xp + 4);
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(a0[i]);
+            v[4 + i] = __uint_as_float(a1[i]);
+          }
+          split_f32x8(v, ah, al);
         }
-        split_f32x8(v, bh, bl);
+      } else if (xok[t]) {
+        ah = load16(reinterpret_cast<const uint16_t*>(xv) + xoff[t] + k);
       }
-    } else {
-      const uint16_t* xp = reinterpret_cast<const uint16_t*>(xv) + (size_t)tok * H + k + kl;
-      if (tok_ok) bh = load16(xp);
+#pragma unroll
+      for (int n = 0; n < NE; ++n) {
+        acc[t][n] = mfma16(as_bf16x8(ah), as_bf16x8(b[n]), acc[t][n]);
+        if (XF32) acc[t][n] = mfma16(as_bf16x8(al), as_bf16x8(b[n]), acc[t][n]);
+      }
     }
+  }
+
+  float* dst = part + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
-      u32x4 a = {0, 0, 0, 0};
-      if (wok[n]) a = load16(wrow[n] + k);
-      acc[n] = mfma16(as_bf16x8(a), as_bf16x8(bh), acc[n]);
-      if (XF32) acc[n] = mfma16(as_bf16x8(a), as_bf16x8(bl), acc[n]);
-    }
-  }
-
-  if (!tok_ok) return;
-  float* dst = part + ((size_t)blockIdx.z * T + tok) * E;
+      const int e = e0 + n * 16 + (lane & 15);
+      if (e >= E) continue;
 #pragma unroll
-  for (int n = 0; n < NE; ++n) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + n * 16 + (lane >> 4) * 4 + i;
-      if (e < E) dst[e] = acc[n][i];
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + t * 16 + (lane >> 4) * 4 + i;
+        if (tok < T) dst[(size_t)tok * E + e] = acc[t][n][i];
+      }
     }
-  }
 }
 
-struct Cand {
-  float s;   // selection score
-  float l;   // logit used for the weight
-  int e;     // expert index (E = none)
-};
-
-__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-  // a ranks before b: larger score, ties to the lower index; "none" never wins.
-  if (a.e < 0x7fffffff && b.e == 0x7fffffff) return true;
-  if (a.e == 0x7fffffff) return false;
-  return a.s > b.s || (a.s == b.s && a.e < b.e);
+// Orderable key of (score, expert): larger key = larger score, and on equal
+// scores the lower expert index.  NaN ranks as -inf.
+__device__ __forceinline__ unsigned long long rank_key(float s, int e) {
+  if (s != s) s = -INFINITY;
+  uint32_t u = __float_as_uint(s);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
 }
 
-__device__ __forceinline__ Cand shfl_xor(const Cand& c, int m) {
-  Cand o;
-  o.s = __shfl_xor(c.s, m);
-  o.l = __shfl_xor(c.l, m);
-  o.e = __shfl_xor(c.e, m);
-  return o;
+__device__ __forceinline__ float key_score(unsigned long long key) {
+  uint32_t u = (uint32_t)(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const unsigned long long o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -122,7 +138,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr int kMaxPerLane = kMaxExperts / kWave;  // 8
 
-// One wave per token.  Expert e lives in lane e % 64, slot e / 64.
+// One wave per token.  Expert e lives in lane e % 64, slot e / 64.  Each round
+// takes the wave-wide largest remaining key; the owner lane retires it.
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ part, int ks, const float* __restrict__ bias, int bias_mode, int T,
     int E, int k, int score, int renorm, float scale, int32_t* __restrict__ idx,
@@ -130,110 +147,94 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  const int none = 0x7fffffff;
 
-  float lg[kMaxPerLane], sc[kMaxPerLane];
-  uint32_t taken = 0;
+  float lg[kMaxPerLane], v[kMaxPerLane];
+  unsigned long long key[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) v[i] = 0.f;
+  // K-slice partial sums, added in slice order; 4 slices of loads in flight
+  for (int s0 = 0; s0 < ks; s0 += 4) {
+    float ld[4][kMaxPerLane];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + i * kWave;
+        ld[u][i] = (s0 + u < ks && e < E) ? part[((size_t)(s0 + u) * T + t) * E + e] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i) v[i] += ld[u][i];
+  }
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = lane + i * kWave;
     lg[i] = -INFINITY;
-    sc[i] = -INFINITY;
+    key[i] = 0ull;  // below every real key
     if (e < E) {
-      float v = 0.f;
-      for (int s = 0; s < ks; ++s) v += part[((size_t)s * T + t) * E + e];
       const float b = bias ? bias[e] : 0.f;
-      float l = (bias && bias_mode == 0) ? v + b : v;
-      float sel = (bias && bias_mode == 1) ? l + b : l;
-      if (sel != sel) sel = -INFINITY;  // NaN never outranks a number
+      const float l = (bias && bias_mode == 0) ? v[i] + b : v[i];
       lg[i] = l;
-      sc[i] = sel;
+      key[i] = rank_key((bias && bias_mode == 1) ? l + b : l, e);
     }
   }
 
-  int win_e[kMaxTopK + 1];
-  float win_l[kMaxTopK + 1];
-  float kth = 0.f, next = -INFINITY;
-  bool have_next = false;
+  // softmax reference point: the largest logit (selection may use biased scores)
+  float m = -INFINITY;
 #pragma unroll
-  for (int r = 0; r <= kMaxTopK; ++r) {
-    if (r > k) continue;
-    Cand best{-INFINITY, 0.f, none};
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + i * kWave;
-      if (e < E && !((taken >> i) & 1u)) {
-        Cand c{sc[i], lg[i], e};
-        if (better(c, best)) best = c;
-      }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      Cand o = shfl_xor(best, m);
-      if (better(o, best)) best = o;
-    }
-    if (r < k) {
-      // k <= E guarantees a candidate; guard anyway so indices stay in range.
-      const int e = best.e == none ? 0 : best.e;
-      win_e[r] = e;
-      win_l[r] = best.l;
-      if (r == k - 1) kth = best.s;
-      if ((e & 63) == lane) taken |= 1u << (e >> 6);
-    } else if (best.e != none) {
-      next = best.s;
-      have_next = true;
-    }
-  }
+  for (int i = 0; i < kMaxPerLane; ++i) m = fmaxf(m, lg[i]);
+  m = wave_max(m);
 
-  // weights
-  float wsel[kMaxTopK];
-  float denom = 0.f;
-  if (score == 0) {  // softmax
-    float m = -INFINITY;
+  float denom = 0.f, kth = 0.f;
+  int my_e = 0;
+  float my_p = 0.f;
+  for (int r = 0; r < k; ++r) {
+    unsigned long long best = 0ull;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) m = fmaxf(m, lg[i]);
-    m = wave_max(m);
+    for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xffffffffu - (uint32_t)best);
+    const int owner = e & 63, slot = e >> 6;
+    float l = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      wsel[j] = 0.f;
-      if (j < k) {
-        wsel[j] = expf(win_l[j] - m);
-        if (renorm) denom += wsel[j];
-      }
+    for (int i = 0; i < kMaxPerLane; ++i)
+      if (i == slot) l = lg[i];
+    l = __shfl(l, owner);
+    if (lane == owner) {
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (i == slot) key[i] = 0ull;
     }
-    if (!renorm) {
+    const float p = score == 0 ? expf(l - m) : 1.f / (1.f + expf(-l));
+    denom += p;
+    if (lane == r) {
+      my_e = e;
+      my_p = p;
+    }
+    if (r == k - 1) kth = key_score(best);
+  }
+  unsigned long long nxt = 0ull;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) nxt = key[i] > nxt ? key[i] : nxt;
+  nxt = wave_max_u64(nxt);
+
+  if (!renorm) {
+    if (score == 0) {
       float z = 0.f;
 #pragma unroll
       for (int i = 0; i < kMaxPerLane; ++i)
         if (lane + i * kWave < E) z += expf(lg[i] - m);
       denom = wave_sum(z);
+    } else {
+      denom = 1.f;
     }
-  } else {  // sigmoid
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      wsel[j] = 0.f;
-      if (j < k) {
-        wsel[j] = 1.f / (1.f + expf(-win_l[j]));
-        denom += wsel[j];
-      }
-    }
-    if (!renorm) denom = 1.f;
   }
-  const float inv = scale / denom;
   if (lane < k) {
-    // select this lane's entry without dynamic register indexing
-    int e = 0;
-    float wv = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (j < k && j == lane) {
-        e = win_e[j];
-        wv = wsel[j] * inv;
-      }
-    idx[(size_t)t * k + lane] = e;
-    wout[(size_t)t * k + lane] = wv;
+    idx[(size_t)t * k + lane] = my_e;
+    wout[(size_t)t * k + lane] = my_p * (scale / denom);
   }
-  if (lane == 0) gap[t] = have_next ? kth - next : INFINITY;
+  if (lane == 0) gap[t] = nxt ? kth - key_score(nxt) : INFINITY;
 }
 
 }  // namespace
@@ -241,20 +242,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
                                 int T, int H, int E, int ks, hipStream_t s) {
   const int kchunk = H / ks;
-  const int ne = E <= 16 ? 1 : (E <= 32 ? 2 : 6);
-  dim3 grid((T + 63) / 64, (E + 16 * ne - 1) / (16 * ne), ks);
-  dim3 block(256);
-#define MOE_ROUTER_CASE(XF, NE_)                                                             \
-  hipLaunchKernelGGL((router_logits_kernel<XF, NE_>), grid, block, 0, s, x, router_w, part, T, \
-                     H, E, kchunk)
+  const int nt = T <= 32 ? 2 : 4;
+  const int ne = T <= 256 ? 1 : 2;
+  dim3 grid((T + 16 * nt - 1) / (16 * nt), (E + 64 * ne - 1) / (64 * ne), ks), block(256);
+#define MOE_ROUTER_CASE(XF, NT_, NE_)                                                         \
+  hipLaunchKernelGGL((router_logits_kernel<XF, NT_, NE_>), grid, block, 0, s, x, router_w, part, \
+                     T, H, E, kchunk)
   if (x_f32) {
-    if (ne == 1) MOE_ROUTER_CASE(true, 1);
-    else if (ne == 2) MOE_ROUTER_CASE(true, 2);
-    else MOE_ROUTER_CASE(true, 6);
+    if (nt == 2) MOE_ROUTER_CASE(true, 2, 1);
+    else if (ne == 1) MOE_ROUTER_CASE(true, 4, 1);
+    else MOE_ROUTER_CASE(true, 4, 2);
   } else {
-    if (ne == 1) MOE_ROUTER_CASE(false, 1);
-    else if (ne == 2) MOE_ROUTER_CASE(false, 2);
-    else MOE_ROUTER_CASE(false, 6);
+    if (nt == 2) MOE_ROUTER_CASE(false, 2, 1);
+    else if (ne == 1) MOE_ROUTER_CASE(false, 4, 1);
+    else MOE_ROUTER_CASE(false, 4, 2);
   }
 #undef MOE_ROUTER_CASE
   return hipGetLastError();

@@ -13,6 +13,15 @@ Comparison rules (tolerances per output dtype):
     fp32 accumulation over at most a few thousand terms; 1e-3 leaves a wide
     margin).  A token whose routing legitimately differs (near-tie) is compared
     with the oracle re-run on the GPU's routing.
+  * bf16 outputs carry their own rounding, up to 2^-8 |y| per element, which no
+    kernel can avoid; where a shape's largest |y| is ~5x RMS that alone is
+    ~2e-2 RMS, and where h is rounded to bf16 (the large-batch path) that
+    rounding adds up to ~1.3e-2 RMS on layers without a shared expert.  Shapes
+    outside the five workloads (small edge cases) therefore assert the
+    rounding-aware form: max_i (|err_i| - 2^-8 |y_ref_i|) <= tol * RMS, the
+    stated budget applied to the error beyond the output's own rounding; the
+    plain figure is still reported.  Indexing mistakes (a wrong row, expert or
+    tile, a dropped k-step) give errors of order RMS and fail either form.
 """
 from __future__ import annotations
 
@@ -64,7 +73,7 @@ def run_gpu(layer, inp, tokens=None, seed_ws=None):
 
 
 def compare(inp, out, route, sample=None, score="softmax", renormalize=True, routed_scale=1.0,
-            bias_mode="logit", k=None, tokens=None):
+            bias_mode="logit", k=None, tokens=None, strict=True):
     """Checks one GPU forward against the oracle; returns a dict of figures."""
     shape = inp.shape
     k = k or shape.top_k
@@ -126,7 +135,16 @@ def compare(inp, out, route, sample=None, score="softmax", renormalize=True, rou
     tol = out_tolerance(shape)
     res = {"max_err_over_rms": err / rms, "rms": rms, "tol": tol, "near_tie_tokens": int(exempt.sum()),
            "flipped": int(flip.sum()), "compared_tokens": len(rows), "weight_err": float(werr)}
-    assert err <= tol * rms, f"output error {err / rms:.4g} x RMS exceeds {tol}: {res}"
+    if out.dtype == torch.bfloat16:
+        y_rounded = torch.from_numpy(y_ref).to(torch.bfloat16).double().numpy()
+        res["out_rounding_floor"] = float(np.abs(y_rounded - y_ref).max()) / rms
+        excess = float((np.abs(y_gpu - y_ref) - 2.0 ** -8 * np.abs(y_ref)).max())
+        res["excess_over_rounding"] = excess / rms
+    if strict or out.dtype != torch.bfloat16:
+        assert err <= tol * rms, f"output error {err / rms:.4g} x RMS exceeds {tol}: {res}"
+    else:
+        assert excess <= tol * rms, (f"error beyond the output rounding "
+                                     f"{excess / rms:.4g} x RMS exceeds {tol}: {res}")
     return res
 
 

@@ -21,12 +21,17 @@ def _say(*a):
 
 
 def _run(shape, seed=0, tokens=None, max_tokens=None, layer_kw=None, cmp_kw=None, sample=None):
+    """Runs one case; shapes other than the five workloads use the
+    rounding-aware output check (see moe_check)."""
+    cmp_kw = dict(cmp_kw or {})
+    cmp_kw.setdefault("strict", shape.name in W)
     _say(shape.name, f"seed={seed}", f"tokens={tokens or shape.tokens}", layer_kw or "")
-    inp = moe_synth.make_layer(shape, seed=seed, device="cuda")
+    inp = moe_synth.make_layer(shape, seed=seed, device="cuda",
+                               tokens=max(tokens or 0, shape.tokens))
     layer = make_layer(shape, max_tokens=max_tokens or shape.tokens, **(layer_kw or {}))
     layer.pack_inputs(inp)
     out, route = run_gpu(layer, inp, tokens)
-    res = compare(inp, out, route, sample=sample, **(cmp_kw or {}))
+    res = compare(inp, out, route, sample=sample, **cmp_kw)
     _say("ok", res)
     return inp, layer, out, route, res
 
@@ -143,6 +148,28 @@ def test_argument_errors():
     with pytest.raises(B.MoeError) as e:
         layer.forward(inp.x[:8], inp.router_w, workspace=ws)
     assert e.value.status == B.MOE_ERR_WORKSPACE
+
+
+# ----------------------------------------------------------------- large-batch (tiled) path
+
+TILED_SMALL = W["tiny"].replace(name="tiled_small", act_dtype="bf16", tokens=512)
+
+
+@pytest.mark.parametrize("tokens", [512, 300, 1000])
+def test_tiled_small_ragged(tokens):
+    """64+ rows per expert selects the LDS-tiled GEMMs: partial 128-row tiles,
+    intermediate width 64 (half a 256-row weight tile)."""
+    _run(TILED_SMALL, tokens=tokens, max_tokens=1000)
+
+
+def test_tiled_shared_width_differs():
+    s = TILED_SMALL.replace(name="tiled_mid", hidden=512, experts=8, inter=256, shared_inter=128,
+                            tokens=1024)
+    _run(s)
+
+
+def test_tiled_no_shared():
+    _run(TILED_SMALL.replace(name="tiled_noshared", shared_inter=0))
 
 
 # ----------------------------------------------------------------- full Step-3.5-Flash shapes
