@@ -107,6 +107,16 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
                         (size_t)(b_ok ? bblk : 0) * nk * 4 * kFragBytes + lane * 16;
 
   const uint16_t* a_base = a_src;
+  // Workgroup barrier without a memory fence: __syncthreads' release fence
+  // would drain every outstanding LDS load, including the stages prefetched
+  // for later steps.  The compiler-only fences keep LDS accesses on their
+  // side; the builtin (unlike an inline-asm s_barrier, which the compiler
+  // must treat as reading every accumulator) does not drain in-flight MFMAs.
+  auto barrier = [] {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
   auto issue = [&](int kk, int stage) {
     uint8_t* st = lds + stage * kStageBytes;
 #pragma unroll
@@ -129,19 +139,23 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
   for (int pass = 0; pass < npass; ++pass) {
     set_rows(pass);
     a_base = pass == 0 ? a_src : h_lo;
-    if (pass > 0) asm volatile("s_barrier" ::: "memory");  // ring free before refilling
+    if (pass > 0) {  // ring free before refilling
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      barrier();
+    }
     issue(0, 0);
     if (nk > 1) issue(1, 1);
     for (int kk = 0; kk < nk; ++kk) {
-      // stage kk must have landed; stage kk+1 (if issued) may still be in flight
-      // (a plain s_barrier: __syncthreads' release fence would drain every
-      // outstanding LDS load, including the stage prefetched for the next step)
+      // stage kk must have landed; stage kk+1 (if issued) may still be in
+      // flight.  s_waitcnt through the builtin (gfx9 encoding: vmcnt bits 3:0
+      // and 15:14, expcnt 6:4, lgkmcnt 11:8) so the compiler sees it.
       if (kk + 1 < nk) {
-        if (b_ok) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+        if (b_ok) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+        else __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
       } else {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
       }
+      barrier();
       if (kk + 2 < nk) issue(kk + 2, (kk + 2) % kStages);
       const uint8_t* st = lds + (kk % kStages) * kStageBytes;
       bf16x8 a[4], b[8];
