@@ -49,6 +49,9 @@ def parse():
                     help="skip timing the oracle on the host (e.g. under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
+                         "reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -142,6 +145,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} bytes 5 times")
+        return
     import moe_synth
     from sparse_mixture_experts_layer_amd import _binding as B
     from sparse_mixture_experts_layer_amd.layer import MoELayer
