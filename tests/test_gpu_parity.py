@@ -201,3 +201,29 @@ def test_int4_decode_32():
 @pytest.mark.parametrize("tokens", [1, 5, 17])
 def test_decode_ragged(tokens):
     _run(W["decode"], tokens=tokens, max_tokens=32)
+
+
+# ----------------------------------------------------------------- further shapes from the pages
+
+STEP3 = W["decode"].replace(name="step3", hidden=7168, experts=48, top_k=3, inter=5120,
+                            shared_inter=5120, renormalize=False, tokens=8)
+
+
+def test_step3_shape_decode():
+    """Step-3's MoE shape (llm-atlas comparison table: hidden 7168, 48 experts,
+    top-3, width 5120, norm_expert_weight false) through the same kernels."""
+    _run(STEP3, cmp_kw=dict(renormalize=False))
+
+
+def test_step3_shape_large_batch_sampled():
+    s = STEP3.replace(name="step3_batch", tokens=1024)      # 64 rows per expert: tiled path
+    _run(s, cmp_kw=dict(renormalize=False), sample=_spread(1024, 12))
+
+
+@pytest.mark.parametrize("tokens", [32, 512])
+def test_dense_ffn_as_one_expert(tokens):
+    """The dense SwiGLU FFN of the first layers (intermediate_size 11264) as a
+    one-expert layer: top-1 of 1 expert with renormalisation gives weight 1."""
+    s = W["decode"].replace(name="dense_ffn", experts=1, top_k=1, inter=11264, shared_inter=0,
+                            tokens=tokens)
+    _run(s, sample=_spread(tokens, 8) if tokens > 64 else None)
