@@ -91,7 +91,9 @@ moe_status_t check_config(const moe_layer_config_t* c) {
 // Per-call plan and workspace layout.
 struct Plan {
   int T, P, ks, tg, max_tiles, has_shared, hstride, tiled;
-  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, h, h_lo, y, total;
+  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, blk_hist, h, h_lo, y,
+      total;
+  int large_dispatch;
 };
 
 Plan make_plan(const moe_layer& L, int T) {
@@ -139,6 +141,9 @@ Plan make_plan(const moe_layer& L, int T) {
   p.row_tok = take((size_t)rows * 4);
   p.tiles = take((size_t)p.max_tiles * 4);
   p.ntiles = take(4);
+  // one workgroup dispatches small batches; larger ones use per-block counts
+  p.large_dispatch = T > 1024;
+  p.blk_hist = take(p.large_dispatch ? (size_t)moe::dispatch_blocks(T) * E * 4 : 0);
   p.h = take((size_t)rows * p.hstride * 4);
   p.h_lo = take(p.tiled && p.has_shared ? (size_t)T * p.hstride * 2 : 0);
   p.y = take((size_t)rows * c.hidden * 4);
@@ -332,9 +337,15 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     e = moe::launch_router_topk(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
                                 c.renormalize, c.routed_scale, idx, wts, gap, stream);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess)
-    e = moe::launch_dispatch(idx, T, k, E, p.has_shared, 16 * p.tg, counts, offsets, perm, inv,
-                             row_tok, tiles, ntiles, stream);
+  if (e == hipSuccess) {
+    if (p.large_dispatch)
+      e = moe::launch_dispatch_large(idx, T, k, E, p.has_shared, 16 * p.tg,
+                                     reinterpret_cast<int32_t*>(ws + p.blk_hist), counts, offsets,
+                                     perm, inv, row_tok, tiles, ntiles, stream);
+    else
+      e = moe::launch_dispatch(idx, T, k, E, p.has_shared, 16 * p.tg, counts, offsets, perm, inv,
+                               row_tok, tiles, ntiles, stream);
+  }
   if (e == hipSuccess) e = mark(2);
   moe::GemmGeom g{};
   g.H = H;

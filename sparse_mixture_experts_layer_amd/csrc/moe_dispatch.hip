@@ -171,7 +171,164 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     for (int t = tid; t < T; t += kDispThreads) row_tok[P + t] = t;
 }
 
+// ---------------------------------------------------------------- large batches
+// Same result, spread over many workgroups: (1) each block of kBlkTokens
+// tokens counts its pairs per expert and per wave; (2) one workgroup turns the
+// block counts into each (block, expert)'s first row and builds the offsets
+// and tile list; (3) each block scatters its pairs with the lane-mask ranks,
+// starting from those rows.  Deterministic: no global atomics.
+constexpr int kBlkWaves = 4;
+constexpr int kBlkTokens = kBlkWaves * kWave;  // one 64-token step per wave
+
+__global__ __launch_bounds__(kBlkWaves * kWave) void dispatch_hist_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ blk_hist) {
+  __shared__ int hist[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kBlkTokens + threadIdx.x;
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      int e = idx[(size_t)t * k + j];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      atomicAdd(&hist[e], 1);
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) blk_hist[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(
+    int32_t* __restrict__ blk_hist, int nblk, int T, int k, int E, int has_shared, int bm,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
+    int32_t* __restrict__ ntiles_out) {
+  __shared__ int tot[kMaxExperts + 1];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int ntile[kMaxExperts + 1];
+  __shared__ int scan_total;
+  const int tid = threadIdx.x;
+  const int P = T * k;
+  constexpr int kChunk = 16;  // block counts loaded together (independent loads)
+  // per expert: total over blocks
+  if (tid < E) {
+    int run = 0;
+    for (int b0 = 0; b0 < nblk; b0 += kChunk) {
+      int c[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        c[i] = b0 + i < nblk ? blk_hist[(size_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) run += c[i];
+    }
+    tot[tid] = run;
+    off[tid] = run;
+  }
+  __syncthreads();
+  block_exclusive_scan(off, &scan_total, E);
+  // each (block, expert) count becomes that block's first row for the expert
+  if (tid < E) {
+    counts[tid] = tot[tid];
+    offsets[tid] = off[tid];
+    ntile[tid] = (tot[tid] + bm - 1) / bm;
+    int run = off[tid];
+    for (int b0 = 0; b0 < nblk; b0 += kChunk) {
+      int c[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        c[i] = b0 + i < nblk ? blk_hist[(size_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        if (b0 + i < nblk) {
+          blk_hist[(size_t)(b0 + i) * E + tid] = run;
+          run += c[i];
+        }
+    }
+  }
+  if (tid == 0) {
+    counts[E] = has_shared ? T : 0;
+    offsets[E] = P;
+    offsets[E + 1] = P + (has_shared ? T : 0);
+    ntile[E] = has_shared ? (T + bm - 1) / bm : 0;
+  }
+  __syncthreads();
+  const int total_tiles = block_exclusive_scan(ntile, &scan_total, E + 1);
+  if (tid <= E) {
+    const int c = tid < E ? tot[tid] : (has_shared ? T : 0);
+    const int nt = (c + bm - 1) / bm;
+    for (int m = 0; m < nt; ++m) tiles[ntile[tid] + m] = (tid << 16) | m;
+  }
+  if (tid == 0) ntiles_out[0] = total_tiles;
+}
+
+__global__ __launch_bounds__(kBlkWaves * kWave) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int has_shared,
+    const int32_t* __restrict__ blk_first, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int32_t* __restrict__ row_tok) {
+  __shared__ int base[kBlkWaves][kMaxExperts];
+  __shared__ unsigned long long mask[kBlkWaves][kMaxExperts];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int P = T * k;
+  for (int i = tid; i < kBlkWaves * E; i += blockDim.x) {
+    base[i / E][i % E] = 0;
+    mask[i / E][i % E] = 0ull;
+  }
+  __syncthreads();
+  const int t = blockIdx.x * kBlkTokens + tid;  // wave w holds tokens 64w .. 64w+63 of the block
+  const bool ok = t < T;
+  int ej[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    ej[j] = 0;
+    if (j < k && ok) {
+      int e = idx[(size_t)t * k + j];
+      ej[j] = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      atomicOr(&mask[wave][ej[j]], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  // first row of each (wave, expert): block start + pairs of earlier waves
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = blk_first[(size_t)blockIdx.x * E + e];
+    for (int w = 0; w < kBlkWaves; ++w) {
+      base[w][e] = run;
+      run += __popcll(mask[w][e]);
+    }
+  }
+  __syncthreads();
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k && ok) {
+      const unsigned long long m = mask[wave][ej[j]];
+      const int row = base[wave][ej[j]] + __popcll(m & below);
+      const int p = t * k + j;
+      perm[row] = p;
+      inv[p] = row;
+      row_tok[row] = t;
+    }
+  }
+  if (has_shared && ok) row_tok[P + t] = t;
+}
+
 }  // namespace
+
+int dispatch_blocks(int T) { return (T + kBlkTokens - 1) / kBlkTokens; }
+
+hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
+                                 int32_t* blk_hist, int32_t* counts, int32_t* offsets,
+                                 int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* tiles,
+                                 int32_t* ntiles, hipStream_t s) {
+  const int nblk = dispatch_blocks(T);
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nblk), dim3(kBlkTokens), 0, s, idx, T, k, E,
+                     blk_hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kDispThreads), 0, s, blk_hist, nblk, T, k,
+                     E, has_shared, bm, counts, offsets, tiles, ntiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(kBlkTokens), 0, s, idx, T, k, E,
+                     has_shared, blk_hist, perm, inv, row_tok);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,

@@ -14,7 +14,10 @@
 // (packed weights), each 1 KiB and each written by one wave-wide
 // global->LDS load in MFMA operand order, so every LDS read is a contiguous
 // 1 KiB ds_read_b128 with no bank conflicts and no register staging.
-// Two stages are in flight while the third is multiplied.
+// Two stages are in flight while the third is multiplied, and the fragments
+// of the next stage are read into registers during the current MFMAs.  Two
+// workgroups share a CU (one wave of each per SIMD), so one's LDS traffic and
+// barrier waits overlap the other's MFMAs.
 //
 // Precision: routed rows keep h in bf16 (one rounding, what the MFMA takes).
 // The shared expert enters the output unweighted, so its rounding error would
@@ -43,9 +46,33 @@ constexpr int kXcds = 8;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
+constexpr int kLoadsPerStage = 6;             // per wave: 2 A + 4 B fragments
+
 // One wave-wide 16-byte-per-lane load into LDS at `lds` (+ 16 * lane).
 __device__ __forceinline__ void load_frag(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)lds, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence: __syncthreads' release fence
+// would drain every outstanding global->LDS load, including the stages
+// prefetched for later steps.  The compiler-only fences keep LDS accesses on
+// their side; the builtin (unlike an inline-asm s_barrier, which the compiler
+// must treat as reading every accumulator) does not drain in-flight MFMAs.
+__device__ __forceinline__ void barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) through the builtin, so the compiler sees it
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__device__ __forceinline__ void wait_vm_lgkm0(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x007C); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0070); break;  // stricter than asked: always safe
+  }
 }
 
 template <int MODE>
@@ -99,35 +126,32 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
       }
     }
   };
-  // this wave's B block (4 fragments, 4 KiB per k-step)
+  // this wave's B block (4 fragments, 4 KiB per k-step).  A wave past the
+  // last block loads block 0 instead (its columns are never stored), so every
+  // wave issues the same number of loads per stage.
   const int bblk = nb * 4 + wave;
-  const bool b_ok = bblk < nblocks;
   const uint8_t* bsrc = g.packed + (size_t)group * g.expert_bytes +
                         (MODE == 0 ? 0 : (size_t)2 * width * H * 2) +
-                        (size_t)(b_ok ? bblk : 0) * nk * 4 * kFragBytes + lane * 16;
+                        (size_t)(bblk < nblocks ? bblk : 0) * nk * 4 * kFragBytes + lane * 16;
 
   const uint16_t* a_base = a_src;
-  // Workgroup barrier without a memory fence: __syncthreads' release fence
-  // would drain every outstanding LDS load, including the stages prefetched
-  // for later steps.  The compiler-only fences keep LDS accesses on their
-  // side; the builtin (unlike an inline-asm s_barrier, which the compiler
-  // must treat as reading every accumulator) does not drain in-flight MFMAs.
-  auto barrier = [] {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  };
   auto issue = [&](int kk, int stage) {
     uint8_t* st = lds + stage * kStageBytes;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
       load_frag(a_base + a_off[f] + (size_t)kk * 32, st + (2 * wave + f) * kFragBytes);
-    if (b_ok) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        load_frag(bsrc + (size_t)kk * 4 * kFragBytes + q * kFragBytes,
-                  st + (kAFrags + 4 * wave + q) * kFragBytes);
-    }
+    for (int q = 0; q < 4; ++q)
+      load_frag(bsrc + (size_t)kk * 4 * kFragBytes + q * kFragBytes,
+                st + (kAFrags + 4 * wave + q) * kFragBytes);
+  };
+  auto rd_a = [&](int stage, int m) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + stage * kStageBytes +
+                                                     (wm * 4 + m) * kFragBytes + lane * 16));
+  };
+  auto rd_b = [&](int stage, int j) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(
+        lds + stage * kStageBytes + (kAFrags + wn * 8 + j) * kFragBytes + lane * 16));
   };
 
   f32x4 acc[4][8];
@@ -136,41 +160,52 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Pipeline, per k-step kk: wait until stage kk+1 has landed (own loads:
+  // vmcnt; everyone's: barrier), refill the ring slot of stage kk (already in
+  // registers) with stage kk+3, then run the MFMAs of stage kk while reading
+  // stage kk+1 from LDS into registers: each B fragment is re-read in place
+  // once its 4 MFMAs are issued, the A fragments go to a second register set.
+  // Global loads of two stages stay in flight.
+  bf16x8 a0[4], a1[4], b[8];
+  auto step = [&](int kk, bf16x8(&ca)[4], bf16x8(&na)[4], bool do_issue, bool do_read, int vm) {
+    wait_vm_lgkm0(vm);
+    barrier();
+    if (do_issue) issue(kk + kStages, kk % kStages);
+    const int nst = (kk + 1) % kStages;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[m][j] = mfma16(ca[m], b[j], acc[m][j]);
+      if (do_read) {
+        b[j] = rd_b(nst, j);
+        if (j < 4) na[j] = rd_a(nst, j);
+      }
+    }
+  };
+  // loads issued after stage kk+1 that may still be in flight at step kk
+  auto vm_at = [&](int kk) { return kk + 2 < nk ? kLoadsPerStage : 0; };
+
   for (int pass = 0; pass < npass; ++pass) {
+    // pass 1 (shared group, down GEMM) starts after the last step's barrier
+    // of pass 0: every wave is done with the ring.
     set_rows(pass);
     a_base = pass == 0 ? a_src : h_lo;
-    if (pass > 0) {  // ring free before refilling
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      barrier();
+    const int pro = nk < kStages ? nk : kStages;
+    for (int s = 0; s < pro; ++s) issue(s, s);
+    wait_vm_lgkm0((pro - 1) * kLoadsPerStage);
+    barrier();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a0[m] = rd_a(0, m);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = rd_b(0, j);
+    int kk = 0;
+    for (; kk + kStages + 1 < nk; kk += 2) {
+      step(kk, a0, a1, true, true, kLoadsPerStage);
+      step(kk + 1, a1, a0, true, true, kLoadsPerStage);
     }
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
-    for (int kk = 0; kk < nk; ++kk) {
-      // stage kk must have landed; stage kk+1 (if issued) may still be in
-      // flight.  s_waitcnt through the builtin (gfx9 encoding: vmcnt bits 3:0
-      // and 15:14, expcnt 6:4, lgkmcnt 11:8) so the compiler sees it.
-      if (kk + 1 < nk) {
-        if (b_ok) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
-        else __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
-      }
-      barrier();
-      if (kk + 2 < nk) issue(kk + 2, (kk + 2) % kStages);
-      const uint8_t* st = lds + (kk % kStages) * kStageBytes;
-      bf16x8 a[4], b[8];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        a[m] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(st + (wm * 4 + m) * kFragBytes + lane * 16));
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + (kAFrags + wn * 8 + j) * kFragBytes +
-                                                          lane * 16));
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
+    for (; kk < nk; kk += 2) {
+      step(kk, a0, a1, kk + kStages < nk, kk + 1 < nk, vm_at(kk));
+      if (kk + 1 < nk) step(kk + 1, a1, a0, kk + 1 + kStages < nk, kk + 2 < nk, vm_at(kk + 1));
     }
   }
 
@@ -210,6 +245,7 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
 
 hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32_t* row_tok,
                                uint16_t* h, uint16_t* h_lo, int hstride, hipStream_t s) {
+  if (16 * g.tg != kTM) return hipErrorInvalidValue;
   const int wmax = g.I > g.Is ? g.I : g.Is;
   const int nblk = (2 * wmax + kTN - 1) / kTN;
   const size_t items = (size_t)g.max_tiles * nblk;
@@ -220,6 +256,7 @@ hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32
 
 hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_t* h_lo,
                              int hstride, float* y, hipStream_t s) {
+  if (16 * g.tg != kTM) return hipErrorInvalidValue;
   const int nblk = (g.H + kTN - 1) / kTN;
   const size_t items = (size_t)g.max_tiles * nblk;
   dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(256);

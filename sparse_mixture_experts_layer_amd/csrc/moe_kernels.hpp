@@ -20,6 +20,14 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int has_shar
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                            int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s);
 
+// Multi-workgroup variant for large batches (same outputs); blk_hist is
+// scratch of dispatch_blocks(T) * E int32.
+int dispatch_blocks(int T);
+hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
+                                 int32_t* blk_hist, int32_t* counts, int32_t* offsets,
+                                 int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* tiles,
+                                 int32_t* ntiles, hipStream_t s);
+
 // ---- grouped expert GEMMs ----------------------------------------------------
 struct GemmGeom {
   int H, I, Is, E, T;         // shapes (T = tokens of this call)

@@ -172,6 +172,26 @@ def test_tiled_no_shared():
     _run(TILED_SMALL.replace(name="tiled_noshared", shared_inter=0))
 
 
+@pytest.mark.parametrize("tokens,inter,shared_inter", [(4000, 96, 160), (3001, 64, 0)])
+def test_tiled_many_rows_per_expert(tokens, inter, shared_inter):
+    """Several hundred rows per expert (as in prefill): many m-tiles per
+    expert, ragged row tails, a weight-block count that leaves a partial
+    column tile (96 -> 3 gate/up blocks of 64), a shared expert wider than
+    the routed ones."""
+    s = TILED_SMALL.replace(name="tiled_deep", inter=inter, shared_inter=shared_inter, tokens=tokens)
+    _run(s)
+
+
+@pytest.mark.parametrize("tokens,act", [(3001, "bf16"), (1537, "f32")])
+def test_large_batch_dispatch(tokens, act):
+    """Past 1024 tokens the dispatch runs over many workgroups (per-block
+    counts, a scan, a per-block scatter); ragged block tails, 64 experts,
+    top-8, compared on every token."""
+    s = W["tiny"].replace(name=f"many_tokens_{act}", experts=64, top_k=8, act_dtype=act,
+                          tokens=tokens)
+    _run(s)
+
+
 # ----------------------------------------------------------------- full Step-3.5-Flash shapes
 
 def _spread(T, n, seed=0):
