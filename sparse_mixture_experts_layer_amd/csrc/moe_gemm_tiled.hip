@@ -24,11 +24,9 @@
 // be the largest term of the output error: its h is stored as bf16 hi + lo
 // (a second plane) and its down GEMM runs a second pass over lo.
 //
-// Tile order: the work list (tile-major, weight blocks fastest) is cut into 8
-// contiguous chunks, one per XCD (workgroups are dealt round-robin over the
-// XCDs), so the m-tiles of one expert run side by side on one XCD and share
-// its L2: an expert's weights are read from HBM about once per N-block
-// instead of once per m-tile.
+// Tile order: the work list (group by group) is cut into 8 contiguous chunks,
+// one per XCD (workgroups are dealt round-robin over the XCDs), so the tiles
+// of one expert run side by side on one XCD and share its L2.
 #include "moe_common.hpp"
 #include "moe_kernels.hpp"
 
@@ -89,11 +87,26 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
   if (slot >= chunk) return;
   const int w = (blockIdx.x % kXcds) * chunk + slot;
   if (w >= total) return;
-  const int tile = w / nblk, nb = w % nblk;
-  const int v = g.tiles[tile];
-  const int group = tile_group(v);
-  const int row0 = g.offsets[group] + tile_m(v) * kTM;
-  const int nrows = min(kTM, g.counts[group] - tile_m(v) * kTM);
+  // Inside a group (expert), gate/up takes the m-tiles as the fastest index,
+  // so the workgroups streaming the same weight block start side by side (the
+  // gathered x rows they also share are few enough to stay in the last-level
+  // cache); down keeps the weight blocks fastest, so the workgroups reading
+  // one tile of h (not cache-resident) run together.
+  const int v0 = g.tiles[w / nblk];
+  const int group = tile_group(v0);
+  int nb, mt;
+  if (MODE == 0) {
+    const int first = w / nblk - tile_m(v0);
+    const int ntg = (g.counts[group] + kTM - 1) / kTM;
+    const int local = w - first * nblk;
+    nb = local / ntg;
+    mt = local % ntg;
+  } else {
+    nb = w % nblk;
+    mt = tile_m(v0);
+  }
+  const int row0 = g.offsets[group] + mt * kTM;
+  const int nrows = min(kTM, g.counts[group] - mt * kTM);
   if (nrows <= 0) return;
   const int width = group == g.E ? g.Is : g.I;
   const int H = g.H;
