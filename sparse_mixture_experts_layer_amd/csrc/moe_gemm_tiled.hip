@@ -24,9 +24,8 @@
 // be the largest term of the output error: its h is stored as bf16 hi + lo
 // (a second plane) and its down GEMM runs a second pass over lo.
 //
-// Tile order: the work list (group by group) is cut into 8 contiguous chunks,
-// one per XCD (workgroups are dealt round-robin over the XCDs), so the tiles
-// of one expert run side by side on one XCD and share its L2.
+// Tile order (which workgroups run together, hence what the L2s and the
+// last-level cache share) differs between the two GEMMs; see the kernel.
 #include "moe_common.hpp"
 #include "moe_kernels.hpp"
 
@@ -40,6 +39,7 @@ constexpr int kAFrags = kTM / 16;             // 8
 constexpr int kBFrags = kTN / 16;             // 16
 constexpr int kStageBytes = (kAFrags + kBFrags) * kFragBytes;  // 24 KiB
 constexpr int kXcds = 8;
+static_assert(4 * 32 * (128 * 4 + 16) <= kStages * kStageBytes, "Y staging fits the ring");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -80,18 +80,26 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
                                                     uint16_t* __restrict__ h_lo, int nblk) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
-  // XCD-contiguous work order
+  // Work order.  Workgroups are dealt round-robin over the 8 XCDs (each with
+  // its own L2; all share the last-level cache).
+  //   gate/up: the work list is cut into 8 contiguous chunks, one per XCD, so
+  //     each XCD runs whole experts; inside an expert the m-tiles are the
+  //     fastest index, so the workgroups streaming one weight block start
+  //     together and share it through L2 (the gathered x rows they also need
+  //     stay in the last-level cache).
+  //   down: plain round-robin with weight blocks fastest, so the 8 XCDs work
+  //     on the same expert at once: its weights are fetched from HBM once
+  //     into the last-level cache, and each XCD keeps only 2 of the 16 weight
+  //     blocks of an expert plus the h tiles in its L2.
   const int total = *g.ntiles * nblk;
-  const int chunk = (total + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= chunk) return;
-  const int w = (blockIdx.x % kXcds) * chunk + slot;
+  int w = (int)blockIdx.x;
+  if (MODE == 0) {
+    const int chunk = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= chunk) return;
+    w = (blockIdx.x % kXcds) * chunk + slot;
+  }
   if (w >= total) return;
-  // Inside a group (expert), gate/up takes the m-tiles as the fastest index,
-  // so the workgroups streaming the same weight block start side by side (the
-  // gathered x rows they also share are few enough to stay in the last-level
-  // cache); down keeps the weight blocks fastest, so the workgroups reading
-  // one tile of h (not cache-resident) run together.
   const int v0 = g.tiles[w / nblk];
   const int group = tile_group(v0);
   int nb, mt;
@@ -223,6 +231,40 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
   }
 
   // epilogue: lane holds rows 4*(lane/16)+i of each 16-row fragment, column lane%16
+  if (MODE == 1) {
+    // fp32 Y goes through LDS so that each lane stores 16 contiguous bytes and
+    // a wave writes whole 512-byte row segments (direct stores from the MFMA
+    // layout would write 64-byte pieces, 4 bytes per lane).  The ring is idle:
+    // every wave passed the last k-step's barrier after its last LDS read.
+    // Each wave stages its 64 x 128 block in two halves of 32 rows in a
+    // private region; rows are padded by 16 bytes against bank conflicts.
+    constexpr int kPitch = 128 * 4 + 16;
+    uint8_t* stg = lds + wave * (32 * kPitch);
+    const int blk0 = nb * 4 + wn * 2;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int lr = mm * 16 + (lane >> 4) * 4 + i, lc = j * 16 + (lane & 15);
+            *reinterpret_cast<float*>(stg + lr * kPitch + lc * 4) = acc[2 * half + mm][j][i];
+          }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int idx = q * kWave + lane, lr = idx >> 5, ch = idx & 31;
+        const f32x4 val = *reinterpret_cast<const f32x4*>(stg + lr * kPitch + ch * 16);
+        const int r = wm * 64 + half * 32 + lr;
+        const int blk = blk0 + (ch >> 4);
+        if (r < nrows && blk < nblocks)
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)(row0 + r) * H +
+                                    blk * 64 + (ch & 15) * 4) = val;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -234,21 +276,15 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
       for (int jb = 0; jb < 2; ++jb) {
         const int blk = nb * 4 + wn * 2 + jb;
         if (blk >= nblocks) continue;
-        if (MODE == 0) {
-          uint16_t* hp = reinterpret_cast<uint16_t*>(out) + row * hstride + blk * 32 + (lane & 15);
+        uint16_t* hp = reinterpret_cast<uint16_t*>(out) + row * hstride + blk * 32 + (lane & 15);
 #pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            const float hv = silu(acc[m][jb * 4 + f][i]) * acc[m][jb * 4 + 2 + f][i];
-            const uint16_t hi = f32_to_bf16_bits(hv);
-            hp[f * 16] = hi;
-            if (shared)
-              h_lo[(row - shared_base) * hstride + blk * 32 + f * 16 + (lane & 15)] =
-                  f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
-          }
-        } else {
-          float* yp = reinterpret_cast<float*>(out) + row * H + blk * 64 + (lane & 15);
-#pragma unroll
-          for (int f = 0; f < 4; ++f) yp[f * 16] = acc[m][jb * 4 + f][i];
+        for (int f = 0; f < 2; ++f) {
+          const float hv = silu(acc[m][jb * 4 + f][i]) * acc[m][jb * 4 + 2 + f][i];
+          const uint16_t hi = f32_to_bf16_bits(hv);
+          hp[f * 16] = hi;
+          if (shared)
+            h_lo[(row - shared_base) * hstride + blk * 32 + f * 16 + (lane & 15)] =
+                f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
         }
       }
     }
