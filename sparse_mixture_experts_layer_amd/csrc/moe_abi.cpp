@@ -102,10 +102,8 @@ Plan make_plan(const moe_layer& L, int T) {
   p.T = T;
   p.P = T * c.top_k;
   p.has_shared = c.shared_inter > 0;
-  // router: split H so that small batches still spread over the CUs (the
-  // grid mirrors launch_router_logits: 16*nt tokens x 64*ne experts per block)
-  const int nt = T <= 32 ? 2 : 4, ne = T <= 256 ? 1 : 2;
-  const int wgs = ((T + 16 * nt - 1) / (16 * nt)) * ((c.num_experts + 64 * ne - 1) / (64 * ne));
+  // router: split H so that small batches still spread over the CUs
+  const int wgs = moe::router_blocks(c.act_dtype == MOE_F32, T, c.num_experts);
   p.ks = 1;
   while (wgs * p.ks < 256 && p.ks < 8 && (c.hidden / 32) % (2 * p.ks) == 0) p.ks *= 2;
   // expert GEMM tile rows: 16 when experts see about one row (decode), 32 or

@@ -26,22 +26,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     ws[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (has_shared) acc = *reinterpret_cast<const f32x4*>(y + (size_t)(P + t) * H + c);
-    for (int j = 0; j < k; ++j) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(y + (size_t)rows[j] * H + c);
-      const float wj = ws[j];
+  // Each thread owns kChunks column groups of 4 per pass, so every row's
+  // loads for all of them are in flight together (bandwidth-bound kernel).
+  constexpr int kChunks = 4;
+  const int stride = blockDim.x * 4;
+  for (int c0 = 0; c0 < H; c0 += stride * kChunks) {
+    f32x4 acc[kChunks];
+    int col[kChunks];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += wj * v[i];
+    for (int i = 0; i < kChunks; ++i) {
+      col[i] = c0 + i * stride + threadIdx.x * 4;
+      acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (has_shared && col[i] < H)
+        acc[i] = *reinterpret_cast<const f32x4*>(y + (size_t)(P + t) * H + col[i]);
     }
-    if (OUT_F32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)t * H + c) = acc;
-    } else {
-      uint2 pk;
-      pk.x = pack_bf16x2(acc[0], acc[1]);
-      pk.y = pack_bf16x2(acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * H + c) = pk;
+    for (int j = 0; j < k; ++j) {
+      const float* yr = y + (size_t)rows[j] * H;
+      const float wj = ws[j];
+      f32x4 v[kChunks];
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i)
+        v[i] = col[i] < H ? *reinterpret_cast<const f32x4*>(yr + col[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] += wj * v[i][e];
+    }
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      if (col[i] >= H) continue;
+      if (OUT_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)t * H + col[i]) = acc[i];
+      } else {
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[i][0], acc[i][1]);
+        pk.y = pack_bf16x2(acc[i][2], acc[i][3]);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * H + col[i]) = pk;
+      }
     }
   }
 }

@@ -8,6 +8,8 @@
 namespace moe {
 
 // ---- router: logits (fp32 partial sums over KS slices of H) + top-k ----------
+// Workgroups of the router logits kernel for a batch (before the K split).
+int router_blocks(bool x_f32, int T, int E);
 hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
                                 int T, int H, int E, int ks, hipStream_t s);
 hipError_t launch_router_topk(const float* part, int ks, const float* bias, int bias_mode, int T,

@@ -100,6 +100,74 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
     }
 }
 
+// Large batches, bf16 x: a workgroup of NW waves covers 16*NT tokens and
+// NW*16*NE experts (all 288 with NT=4, NE=6, NW=3), so per k-step a wave loads
+// NT + NE fragments for NT*NE MFMAs (the NT x fragments are shared by the
+// workgroup's waves through L1).  The loads of step k+32 are issued before
+// the MFMAs of step k.  Rows past T or E read row 0; their results are never
+// stored.  kchunk / 32 must be even.
+template <int NT, int NE, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void router_logits_wide_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ part,
+    int T, int H, int E, int kchunk) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * 16 * NT;
+  const int e0 = (blockIdx.y * NW + wave) * 16 * NE;
+  if (e0 >= E) return;
+  const int kbeg = blockIdx.z * kchunk, kend = kbeg + kchunk;
+  const int kl = (lane >> 4) * 8;
+  const uint16_t* xrow[NT];
+  const uint16_t* wrow[NE];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tok = t0 + t * 16 + (lane & 15);
+    xrow[t] = x + (size_t)(tok < T ? tok : 0) * H + kl;
+  }
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+    const int e = e0 + n * 16 + (lane & 15);
+    wrow[n] = wr + (size_t)(e < E ? e : 0) * H + kl;
+  }
+  f32x4 acc[NT][NE];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int n = 0; n < NE; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 a0[NT], b0[NE], a1[NT], b1[NE];
+  auto load = [&](u32x4(&a)[NT], u32x4(&b)[NE], int k) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) a[t] = load16(xrow[t] + k);
+#pragma unroll
+    for (int n = 0; n < NE; ++n) b[n] = load16(wrow[n] + k);
+  };
+  auto mma = [&](const u32x4(&a)[NT], const u32x4(&b)[NE]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int n = 0; n < NE; ++n) acc[t][n] = mfma16(as_bf16x8(a[t]), as_bf16x8(b[n]), acc[t][n]);
+  };
+  load(a0, b0, kbeg);
+  for (int k = kbeg; k < kend; k += 64) {
+    load(a1, b1, k + 32);
+    mma(a0, b0);
+    if (k + 64 < kend) load(a0, b0, k + 64);
+    mma(a1, b1);
+  }
+  float* dst = part + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+      const int e = e0 + n * 16 + (lane & 15);
+      if (e >= E) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + t * 16 + (lane >> 4) * 4 + i;
+        if (tok < T) dst[(size_t)tok * E + e] = acc[t][n][i];
+      }
+    }
+}
+
 // Orderable key of (score, expert): larger key = larger score, and on equal
 // scores the lower expert index.  NaN ranks as -inf.
 __device__ __forceinline__ unsigned long long rank_key(float s, int e) {
@@ -239,22 +307,46 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 
 }  // namespace
 
+// Launch shape of the logits kernel for a batch: 16*nt tokens x 16*ne*nw
+// experts per workgroup.
+namespace {
+struct RouterShape {
+  int nt, ne, nw;
+  bool wide;
+};
+RouterShape router_shape(bool x_f32, int T, int ksteps) {
+  if (!x_f32 && T > 256 && ksteps % 2 == 0) return {4, 6, 3, true};
+  return {T <= 32 ? 2 : 4, T <= 256 ? 1 : 2, 4, false};
+}
+}  // namespace
+
+int router_blocks(bool x_f32, int T, int E) {
+  const RouterShape r = router_shape(x_f32, T, 2);
+  return ((T + 16 * r.nt - 1) / (16 * r.nt)) * ((E + 16 * r.ne * r.nw - 1) / (16 * r.ne * r.nw));
+}
+
 hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
                                 int T, int H, int E, int ks, hipStream_t s) {
   const int kchunk = H / ks;
-  const int nt = T <= 32 ? 2 : 4;
-  const int ne = T <= 256 ? 1 : 2;
-  dim3 grid((T + 16 * nt - 1) / (16 * nt), (E + 64 * ne - 1) / (64 * ne), ks), block(256);
+  // the wide kernel takes an even number of 32-wide k-steps per slice
+  const RouterShape r = router_shape(x_f32, T, kchunk / 32);
+  dim3 grid((T + 16 * r.nt - 1) / (16 * r.nt), (E + 16 * r.ne * r.nw - 1) / (16 * r.ne * r.nw), ks);
+  if (r.wide) {
+    hipLaunchKernelGGL((router_logits_wide_kernel<4, 6, 3>), grid, dim3(64 * 3), 0, s,
+                       static_cast<const uint16_t*>(x), router_w, part, T, H, E, kchunk);
+    return hipGetLastError();
+  }
+  dim3 block(256);
 #define MOE_ROUTER_CASE(XF, NT_, NE_)                                                         \
   hipLaunchKernelGGL((router_logits_kernel<XF, NT_, NE_>), grid, block, 0, s, x, router_w, part, \
                      T, H, E, kchunk)
   if (x_f32) {
-    if (nt == 2) MOE_ROUTER_CASE(true, 2, 1);
-    else if (ne == 1) MOE_ROUTER_CASE(true, 4, 1);
+    if (r.nt == 2) MOE_ROUTER_CASE(true, 2, 1);
+    else if (r.ne == 1) MOE_ROUTER_CASE(true, 4, 1);
     else MOE_ROUTER_CASE(true, 4, 2);
   } else {
-    if (nt == 2) MOE_ROUTER_CASE(false, 2, 1);
-    else if (ne == 1) MOE_ROUTER_CASE(false, 4, 1);
+    if (r.nt == 2) MOE_ROUTER_CASE(false, 2, 1);
+    else if (r.ne == 1) MOE_ROUTER_CASE(false, 4, 1);
     else MOE_ROUTER_CASE(false, 4, 2);
   }
 #undef MOE_ROUTER_CASE
