@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
 //   gate/up scales [W/32][H/128][16 rows][4 blocks][4 kg] fp16     W*H/8 bytes
 //   down q         [H/64][W/128][f0..f3][64][16 B]                 H*W/2 bytes
 //   down scales    [H/64][W/128][16 rows][4 blocks][4 kg] fp16     H*W/16 bytes
-// MODE 0: gate/up (A = gathered x); MODE 1: down (A = h fp32 rounded to bf16).
+// MODE 0: gate/up (A = gathered x), h stored as bf16; MODE 1: down (A = bf16 h).
 constexpr uint32_t kMinus136x2 = 0xC308C308u;  // bf16 -136 in both halves
 
 template <int MODE, bool XF32, int TG>
@@ -232,8 +232,8 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
                                                           const int32_t* __restrict__ row_tok,
                                                           float* __restrict__ out, int hstride,
                                                           int nblk) {
-  constexpr bool AF32 = MODE == 1 ? true : XF32;
-  constexpr bool SPLIT = MODE == 0 && XF32;   // down rounds h to bf16 (one MFMA per block)
+  constexpr bool AF32 = MODE == 1 ? false : XF32;  // h is stored as bf16
+  constexpr bool SPLIT = MODE == 0 && XF32;
   const int tile = blockIdx.x / nblk, nb = blockIdx.x % nblk;
   TileInfo ti;
   if (!tile_info(g, tile, ti)) return;
@@ -270,12 +270,19 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 q[4], qn[4], s[2], sn[2];
+  // Weight blocks (and their scales) are loaded two blocks ahead, activations
+  // one block ahead: the packed INT4 stream is a quarter of the bf16 bytes per
+  // MFMA, so more of it must be in flight to cover HBM latency.
+  u32x4 q[4], qn[4], qn2[4], s[2], sn[2], sn2[2];
   ARow<AF32> a[4][TG], an[4][TG];
+  auto load_q = [&](u32x4(&qq)[4], u32x4(&ss)[2], int kb) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) q[j] = load16_stream(qp + j * kFragBytes);
-  s[0] = load16_stream(sp);
-  s[1] = load16_stream(sp + 16);
+    for (int j = 0; j < 4; ++j) qq[j] = load16_stream(qp + (size_t)kb * kBlockBytes + j * kFragBytes);
+    ss[0] = load16_stream(sp + (size_t)kb * 512);
+    ss[1] = load16_stream(sp + (size_t)kb * 512 + 16);
+  };
+  load_q(q, s, 0);
+  if (nkb > 1) load_q(qn, sn, 1);
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
@@ -283,12 +290,8 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
 
   for (int kb = 0; kb < nkb; ++kb) {
     const bool more = kb + 1 < nkb;
+    if (kb + 2 < nkb) load_q(qn2, sn2, kb + 2);
     if (more) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        qn[j] = load16_stream(qp + (size_t)(kb + 1) * kBlockBytes + j * kFragBytes);
-      sn[0] = load16_stream(sp + (size_t)(kb + 1) * 512);
-      sn[1] = load16_stream(sp + (size_t)(kb + 1) * 512 + 16);
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
@@ -322,9 +325,14 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
       }
     if (more) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) q[j] = qn[j];
+      for (int j = 0; j < 4; ++j) {
+        q[j] = qn[j];
+        qn[j] = qn2[j];
+      }
       s[0] = sn[0];
       s[1] = sn[1];
+      sn[0] = sn2[0];
+      sn[1] = sn2[1];
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
@@ -340,9 +348,11 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
       if (r >= ti.nrows) continue;
       const size_t row = (size_t)ti.row0 + r;
       if (MODE == 0) {
+        uint16_t* hb = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
         for (int f = 0; f < 2; ++f)
-          out[row * hstride + f0 + f * 16 + (lane & 15)] = silu(acc[t][f][i]) * acc[t][2 + f][i];
+          hb[row * hstride + f0 + f * 16 + (lane & 15)] =
+              f32_to_bf16_bits(silu(acc[t][f][i]) * acc[t][2 + f][i]);
       } else {
 #pragma unroll
         for (int f = 0; f < 4; ++f) out[row * H + f0 + f * 16 + (lane & 15)] = acc[t][f][i];
