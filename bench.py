@@ -30,7 +30,11 @@ METRIC = "MoE-layer tokens/s + % of HBM BW (decode) / % of bf16 MFMA peak (prefi
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E (published)
 PEAK_BF16 = 2.5e15         # flop/s, MI355X dense bf16 MFMA (published)
 PROFILES = os.path.join(ROOT, "profiles")
-GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_layer_amd", "csrc", "moe_gemm_stream.hip")
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_layer_amd", "csrc")
+# source of the dominant (gate/up) kernel per workload: LDS-tiled GEMMs for the
+# prefill batch, weight-streaming GEMMs for the decode-sized ones
+GEMM_SRC = {"prefill": os.path.join(CSRC, "moe_gemm_tiled.hip")}
+GEMM_SRC_DEFAULT = os.path.join(CSRC, "moe_gemm_stream.hip")
 
 
 def log(*a):
@@ -74,7 +78,7 @@ def read_counters(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("src_sha") != src_digest(GEMM_SRC):
+    if kv.get("src_sha") != src_digest(GEMM_SRC.get(workload, GEMM_SRC_DEFAULT)):
         return None
     try:
         return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
