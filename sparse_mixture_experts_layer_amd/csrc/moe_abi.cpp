@@ -143,7 +143,9 @@ Plan make_plan(const moe_layer& L, int T) {
   p.large_dispatch = T > 1024;
   p.blk_hist = take(p.large_dispatch ? (size_t)moe::dispatch_blocks(T) * E * 4 : 0);
   p.h = take((size_t)rows * p.hstride * 4);
-  p.h_lo = take(p.tiled && p.has_shared ? (size_t)T * p.hstride * 2 : 0);
+  // bf16 remainder of the shared expert's h: bf16 weights and activations
+  const bool lo_plane = p.has_shared && c.weight_dtype == MOE_BF16 && c.act_dtype == MOE_BF16;
+  p.h_lo = take(lo_plane ? (size_t)T * p.hstride * 2 : 0);
   p.y = take((size_t)rows * c.hidden * 4);
   p.total = o;
   return p;
@@ -368,9 +370,11 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = moe::launch_down_tiled(g, hb, hl, p.hstride, y, stream);
   } else {
-    if (e == hipSuccess) e = moe::launch_gateup(g, int4, f32, x, row_tok, h, p.hstride, stream);
+    uint16_t* hl = reinterpret_cast<uint16_t*>(ws + p.h_lo);
+    if (e == hipSuccess)
+      e = moe::launch_gateup(g, int4, f32, x, row_tok, h, hl, p.hstride, stream);
     if (e == hipSuccess) e = mark(3);
-    if (e == hipSuccess) e = moe::launch_down(g, int4, h, p.hstride, y, stream);
+    if (e == hipSuccess) e = moe::launch_down(g, int4, f32, h, hl, p.hstride, y, stream);
   }
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)

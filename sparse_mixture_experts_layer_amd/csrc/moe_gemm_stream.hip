@@ -118,19 +118,34 @@ struct TileRows {
 };
 
 // ------------------------------------------------------------------ bf16 weights
-// MODE 0: gate/up (A = gathered x, fp32 or bf16; out h fp32 with SiLU*up)
-// MODE 1: down    (A = h fp32 split hi+lo; out Y fp32)
+// MODE 0: gate/up (A = gathered x, fp32 or bf16; out h with SiLU*up)
+// MODE 1: down    (A = h; out Y fp32)
+// HM (h format): 0 = fp32 h, entering the down MFMA as hi + lo (layers with fp32
+// activations, whose fp32 output is held to a tight bound); 1 = bf16 h for the
+// routed rows, 2 = bf16 h plus a bf16 remainder plane h_lo for the shared
+// expert's rows (layers with bf16 activations: the routed terms are weighted
+// by ~1/k, the unweighted shared expert keeps its h to ~16 bits).  In the down
+// GEMM, HM 1 runs the routed tiles and HM 2 the shared tiles, the latter with
+// one more MFMA per k-step over h_lo; HM 3 runs both in one launch (the
+// shared tiles alone are too few to fill the GPU at decode batch sizes).
 // Packed block of a wave: gate/up [W/32][H/32][g0 g1 u0 u1]; down [H/64][W/32][f0..f3].
-template <int MODE, bool XF32, int TG, int U>
+template <int MODE, bool XF32, int TG, int U, int HM>
 __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void* __restrict__ a_src,
                                                           const int32_t* __restrict__ row_tok,
                                                           float* __restrict__ out, int hstride,
-                                                          int nblk) {
-  constexpr bool AF32 = MODE == 1 ? true : XF32;
-  constexpr bool SPLIT = AF32;  // fp32 A rows always enter as hi + lo
-  const int tile = blockIdx.x / nblk, nb = blockIdx.x % nblk;
+                                                          uint16_t* __restrict__ h_lo, int nblk) {
+  constexpr bool AF32 = MODE == 1 ? HM == 0 : XF32;
+  constexpr bool SPLIT = AF32;            // fp32 A rows always enter as hi + lo
+  constexpr bool LO = MODE == 1 && (HM == 2 || HM == 3);  // h_lo operand compiled in
+  // down with HM 2 walks the shared group's tiles only (the last ones of the list)
+  const int nsh = MODE == 1 && HM == 2 ? (g.T + 16 * TG - 1) / (16 * TG) : 0;
+  const int tile = nsh ? *g.ntiles - nsh + (int)(blockIdx.x / nblk) : (int)(blockIdx.x / nblk);
+  const int nb = blockIdx.x % nblk;
   TileInfo ti;
   if (!tile_info(g, tile, ti)) return;
+  if (MODE == 1 && HM == 1 && ti.group == g.E) return;  // shared tiles: the HM 2 launch
+  if (MODE == 1 && HM == 2 && ti.group != g.E) return;
+  const bool lo = LO && ti.group == g.E;  // workgroup-uniform
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = g.H;
   int f0, K;
@@ -157,14 +172,25 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // remainder rows of the shared expert: h_lo row = permuted row - first shared row
+  size_t lo_off[TG];
+  if (lo) {
+#pragma unroll
+    for (int t = 0; t < TG; ++t) lo_off[t] = rows.off[t] - (size_t)g.offsets[g.E] * hstride;
+  }
+  constexpr int NL = LO ? 1 : 0;
   u32x4 w[U][4], wn[U][4];
   ARow<AF32> a[U][TG], an[U][TG];
+  ARow<false> l[U][TG * NL + 1 - NL], ln[U][TG * NL + 1 - NL];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[u][j] = load16_stream(wp + (size_t)u * kBlockBytes + j * kFragBytes);
 #pragma unroll
-    for (int t = 0; t < TG; ++t) a[u][t].load(a_src, rows.off[t] + u * 32, rows.ok[t]);
+    for (int t = 0; t < TG; ++t) {
+      a[u][t].load(a_src, rows.off[t] + u * 32, rows.ok[t]);
+      if (lo) l[u][t].load(h_lo, lo_off[t] + u * 32, rows.ok[t]);
+    }
   }
   for (int k0 = 0; k0 < nk; k0 += U) {
     const bool more = k0 + U < nk;
@@ -175,8 +201,10 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
         for (int j = 0; j < 4; ++j)
           wn[u][j] = load16_stream(wp + (size_t)(k0 + U + u) * kBlockBytes + j * kFragBytes);
 #pragma unroll
-        for (int t = 0; t < TG; ++t)
+        for (int t = 0; t < TG; ++t) {
           an[u][t].load(a_src, rows.off[t] + (size_t)(k0 + U + u) * 32, rows.ok[t]);
+          if (lo) ln[u][t].load(h_lo, lo_off[t] + (size_t)(k0 + U + u) * 32, rows.ok[t]);
+        }
       }
     }
 #pragma unroll
@@ -187,6 +215,12 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
         a[u][t].operands(ah, al);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[t][j] = mma<SPLIT>(ah, al, as_bf16x8(w[u][j]), acc[t][j]);
+        if (lo) {
+          bf16x8 lh, ll;
+          l[u][t].operands(lh, ll);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[t][j] = mfma16(lh, as_bf16x8(w[u][j]), acc[t][j]);
+        }
       }
     if (more) {
 #pragma unroll
@@ -194,7 +228,10 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[u][j] = wn[u][j];
 #pragma unroll
-        for (int t = 0; t < TG; ++t) a[u][t] = an[u][t];
+        for (int t = 0; t < TG; ++t) {
+          a[u][t] = an[u][t];
+          if (lo) l[u][t] = ln[u][t];
+        }
       }
     }
   }
@@ -207,10 +244,22 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
       const int r = t * 16 + (lane >> 4) * 4 + i;
       if (r >= ti.nrows) continue;
       const size_t row = (size_t)ti.row0 + r;
-      if (MODE == 0) {
+      if (MODE == 0 && HM == 0) {
 #pragma unroll
         for (int f = 0; f < 2; ++f)
           out[row * hstride + f0 + f * 16 + (lane & 15)] = silu(acc[t][f][i]) * acc[t][2 + f][i];
+      } else if (MODE == 0) {
+        uint16_t* hb = reinterpret_cast<uint16_t*>(out);
+        const bool shared = ti.group == g.E;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float hv = silu(acc[t][f][i]) * acc[t][2 + f][i];
+          const uint16_t hi = f32_to_bf16_bits(hv);
+          hb[row * hstride + f0 + f * 16 + (lane & 15)] = hi;
+          if (shared)
+            h_lo[(row - g.offsets[g.E]) * hstride + f0 + f * 16 + (lane & 15)] =
+                f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
+        }
       } else {
 #pragma unroll
         for (int f = 0; f < 4; ++f) out[row * H + f0 + f * 16 + (lane & 15)] = acc[t][f][i];
@@ -361,52 +410,78 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
 }
 
 template <int MODE, int TG>
-hipError_t launch_mode(const GemmGeom& g, bool int4, bool f32, const void* a,
-                       const int32_t* row_tok, float* out, int hstride, hipStream_t s) {
+hipError_t launch_mode(const GemmGeom& g, bool int4, bool act_f32, const void* a,
+                       const int32_t* row_tok, float* out, uint16_t* h_lo, int hstride,
+                       hipStream_t s) {
   const int wmax = g.I > g.Is ? g.I : g.Is;
   const int nblk = MODE == 0 ? (wmax + 127) / 128 : (g.H + 255) / 256;
   dim3 grid((unsigned)g.max_tiles * nblk), block(256);
-#define MOE_L(KERNEL) \
-  hipLaunchKernelGGL(KERNEL, grid, block, 0, s, g, a, row_tok, out, hstride, nblk)
   if (int4) {
-    if (f32) MOE_L((stream_int4_kernel<MODE, true, TG>));
-    else MOE_L((stream_int4_kernel<MODE, false, TG>));
+    if (act_f32 && MODE == 0)
+      hipLaunchKernelGGL((stream_int4_kernel<MODE, true, TG>), grid, block, 0, s, g, a, row_tok,
+                         out, hstride, nblk);
+    else
+      hipLaunchKernelGGL((stream_int4_kernel<MODE, false, TG>), grid, block, 0, s, g, a, row_tok,
+                         out, hstride, nblk);
+    return hipGetLastError();
+  }
+#define MOE_L(GRID, ...)                                                                         \
+  hipLaunchKernelGGL((stream_bf16_kernel<__VA_ARGS__>), GRID, block, 0, s, g, a, row_tok, out, \
+                     hstride, h_lo, nblk)
+  if constexpr (MODE == 0) {
+    if (act_f32) MOE_L(grid, MODE, true, TG, 2, 0);
+    else MOE_L(grid, MODE, false, TG, 2, 1);
+    return hipGetLastError();
   } else {
-    // k-steps per group: 2 when every group's K/32 is even (H % 64 == 0 always;
-    // the expert widths are only multiples of 32)
-    const bool even = MODE == 0 || ((g.I / 32) % 2 == 0 && (g.Is / 32) % 2 == 0);
-    if (even) {
-      if (f32) MOE_L((stream_bf16_kernel<MODE, true, TG, 2>));
-      else MOE_L((stream_bf16_kernel<MODE, false, TG, 2>));
+    // down: k-steps per group 2 when every group's K/32 is even (the expert
+    // widths are only multiples of 32)
+    const bool even = (g.I / 32) % 2 == 0 && (g.Is / 32) % 2 == 0;
+    const int nsh = g.Is > 0 ? (g.T + 16 * TG - 1) / (16 * TG) : 0;
+    dim3 grid_sh((unsigned)nsh * nblk);
+    if (act_f32) {
+      if (even) MOE_L(grid, MODE, false, TG, 2, 0);
+      else MOE_L(grid, MODE, false, TG, 1, 0);
+      return hipGetLastError();
+    }
+    if constexpr (TG == 1) {  // decode-sized: one launch for routed and shared tiles
+      if (even) MOE_L(grid, MODE, false, TG, 2, 3);
+      else MOE_L(grid, MODE, false, TG, 1, 3);
+      return hipGetLastError();
     } else {
-      if (f32) MOE_L((stream_bf16_kernel<MODE, true, TG, 1>));
-      else MOE_L((stream_bf16_kernel<MODE, false, TG, 1>));
+      if (even) MOE_L(grid, MODE, false, TG, 2, 1);
+      else MOE_L(grid, MODE, false, TG, 1, 1);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || nsh == 0) return e;
+      if (even) MOE_L(grid_sh, MODE, false, TG, 2, 2);
+      else MOE_L(grid_sh, MODE, false, TG, 1, 2);
+      return hipGetLastError();
     }
   }
 #undef MOE_L
-  return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t launch_tg(const GemmGeom& g, bool int4, bool f32, const void* a,
-                     const int32_t* row_tok, float* out, int hstride, hipStream_t s) {
+hipError_t launch_tg(const GemmGeom& g, bool int4, bool act_f32, const void* a,
+                     const int32_t* row_tok, float* out, uint16_t* h_lo, int hstride,
+                     hipStream_t s) {
   switch (g.tg) {
-    case 1: return launch_mode<MODE, 1>(g, int4, f32, a, row_tok, out, hstride, s);
-    case 2: return launch_mode<MODE, 2>(g, int4, f32, a, row_tok, out, hstride, s);
-    default: return launch_mode<MODE, 4>(g, int4, f32, a, row_tok, out, hstride, s);
+    case 1: return launch_mode<MODE, 1>(g, int4, act_f32, a, row_tok, out, h_lo, hstride, s);
+    case 2: return launch_mode<MODE, 2>(g, int4, act_f32, a, row_tok, out, h_lo, hstride, s);
+    default: return launch_mode<MODE, 4>(g, int4, act_f32, a, row_tok, out, h_lo, hstride, s);
   }
 }
 
 }  // namespace
 
 hipError_t launch_gateup(const GemmGeom& g, bool int4, bool act_f32, const void* x,
-                         const int32_t* row_tok, float* h, int hstride, hipStream_t s) {
-  return launch_tg<0>(g, int4, act_f32, x, row_tok, h, hstride, s);
+                         const int32_t* row_tok, void* h, uint16_t* h_lo, int hstride,
+                         hipStream_t s) {
+  return launch_tg<0>(g, int4, act_f32, x, row_tok, static_cast<float*>(h), h_lo, hstride, s);
 }
 
-hipError_t launch_down(const GemmGeom& g, bool int4, const float* h, int hstride, float* y,
-                       hipStream_t s) {
-  return launch_tg<1>(g, int4, true, h, nullptr, y, hstride, s);
+hipError_t launch_down(const GemmGeom& g, bool int4, bool act_f32, const void* h,
+                       const uint16_t* h_lo, int hstride, float* y, hipStream_t s) {
+  return launch_tg<1>(g, int4, act_f32, h, nullptr, y, const_cast<uint16_t*>(h_lo), hstride, s);
 }
 
 }  // namespace moe

@@ -43,12 +43,17 @@ struct GemmGeom {
   int tg;                     // token groups of 16 per tile (tile rows = 16 * tg)
 };
 
-// h[row][f] = silu(x W_gate^T) * (x W_up^T) (fp32) for every permuted row.
+// h[row][f] = silu(x W_gate^T) * (x W_up^T) for every permuted row; h is fp32
+// when the activations are fp32 (bf16 weights), bf16 otherwise, with the shared
+// expert's rows also leaving a bf16 remainder in h_lo ([T][hstride]; bf16
+// weights only).
 hipError_t launch_gateup(const GemmGeom& g, bool int4, bool act_f32, const void* x,
-                         const int32_t* row_tok, float* h, int hstride, hipStream_t s);
-// Y[row][:] = h[row] W_down^T (fp32; h split into bf16 hi + lo) for every permuted row.
-hipError_t launch_down(const GemmGeom& g, bool int4, const float* h, int hstride, float* y,
-                       hipStream_t s);
+                         const int32_t* row_tok, void* h, uint16_t* h_lo, int hstride,
+                         hipStream_t s);
+// Y[row][:] = h[row] W_down^T (fp32) for every permuted row, h as left by
+// launch_gateup (fp32 h enters the MFMA as bf16 hi + lo).
+hipError_t launch_down(const GemmGeom& g, bool int4, bool act_f32, const void* h,
+                       const uint16_t* h_lo, int hstride, float* y, hipStream_t s);
 
 // Large-batch (MFMA-bound) variants: 128-row tiles (g.tg must be 8), bf16 h;
 // the shared group's h also gets a bf16 remainder plane h_lo ([T][hstride]).
