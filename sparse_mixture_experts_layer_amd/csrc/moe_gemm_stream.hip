@@ -319,34 +319,42 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Weight blocks (and their scales) are loaded two blocks ahead, activations
-  // one block ahead: the packed INT4 stream is a quarter of the bf16 bytes per
-  // MFMA, so more of it must be in flight to cover HBM latency.
-  u32x4 q[4], qn[4], qn2[4], s[2], sn[2], sn2[2];
-  ARow<AF32> a[4][TG], an[4][TG];
-  auto load_q = [&](u32x4(&qq)[4], u32x4(&ss)[2], int kb) {
+  // Blocks of 128 k (4 weight fragments, their scales, the A rows) rotate
+  // through three register sets, loaded two blocks ahead: the packed INT4
+  // stream is a quarter of the bf16 bytes per MFMA, so more of it must be in
+  // flight to cover HBM latency.  The loop is unrolled by three so the sets
+  // are never copied (a copy would wait for the loads just issued), and every
+  // load is unconditional (past the last block the last one is re-read; rows
+  // past the tile read a valid row whose results are never stored), which
+  // keeps the compiler's wait counts exact.
+  struct Blk {
+    u32x4 q[4], s[2];
+    ARow<AF32> a[4][TG];
+  } b0, b1, b2;
+  auto load_blk = [&](Blk& b, int kb) {
+    kb = kb < nkb ? kb : nkb - 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qq[j] = load16_stream(qp + (size_t)kb * kBlockBytes + j * kFragBytes);
-    ss[0] = load16_stream(sp + (size_t)kb * 512);
-    ss[1] = load16_stream(sp + (size_t)kb * 512 + 16);
+    for (int j = 0; j < 4; ++j) b.q[j] = load16_stream(qp + (size_t)kb * kBlockBytes + j * kFragBytes);
+    b.s[0] = load16_stream(sp + (size_t)kb * 512);
+    b.s[1] = load16_stream(sp + (size_t)kb * 512 + 16);
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+      for (int t = 0; t < TG; ++t) b.a[kg][t].load(a_src, rows.off[t] + (size_t)kb * 128 + kg * 32, true);
   };
-  load_q(q, s, 0);
-  if (nkb > 1) load_q(qn, sn, 1);
-#pragma unroll
-  for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-    for (int t = 0; t < TG; ++t) a[kg][t].load(a_src, rows.off[t] + kg * 32, rows.ok[t]);
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (kb + 2 < nkb) load_q(qn2, sn2, kb + 2);
-    if (more) {
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-        for (int t = 0; t < TG; ++t)
-          an[kg][t].load(a_src, rows.off[t] + (size_t)(kb + 1) * 128 + kg * 32, rows.ok[t]);
-    }
+  // 8 nibbles -> 8 bf16 (128 + u): the OR constant sits in a register so each
+  // pair is one v_and_or_b32 (a VOP3 cannot take two literals)
+  uint32_t c4300;
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(c4300));
+  auto widen = [c4300](uint32_t w) {
+    u32x4 r;
+    r[0] = (w & 0x000f000fu) | c4300;
+    r[1] = ((w >> 4) & 0x000f000fu) | c4300;
+    r[2] = ((w >> 8) & 0x000f000fu) | c4300;
+    r[3] = ((w >> 12) & 0x000f000fu) | c4300;
+    return as_bf16x8(r);
+  };
+  auto compute = [&](const Blk& b) {
     // scales of this lane's weight row: [4 blocks][4 kg] fp16
     float sc[4][4];
 #pragma unroll
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg) {
         const int e = j * 4 + kg;
-        const uint32_t word = s[e >> 3][(e >> 1) & 3];
+        const uint32_t word = b.s[e >> 3][(e >> 1) & 3];
         const uint16_t bits = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
         sc[j][kg] = (float)__builtin_bit_cast(_Float16, bits);
       }
@@ -363,31 +371,33 @@ __global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void
 #pragma unroll
       for (int t = 0; t < TG; ++t) {
         bf16x8 ah, al;
-        a[kg][t].operands(ah, al);
+        b.a[kg][t].operands(ah, al);
         const f32x4 corr = mma<SPLIT>(ah, al, m136, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 p = mma<SPLIT>(ah, al, int4_to_bf16x8_biased(q[j][kg]), corr);
+          const f32x4 p = mma<SPLIT>(ah, al, widen(b.q[j][kg]), corr);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[t][j][i] += sc[j][kg] * p[i];
         }
       }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        q[j] = qn[j];
-        qn[j] = qn2[j];
-      }
-      s[0] = sn[0];
-      s[1] = sn[1];
-      sn[0] = sn2[0];
-      sn[1] = sn2[1];
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-        for (int t = 0; t < TG; ++t) a[kg][t] = an[kg][t];
-    }
+  };
+  load_blk(b0, 0);
+  load_blk(b1, 1);
+  int kb = 0;
+  for (; kb + 3 <= nkb; kb += 3) {
+    load_blk(b2, kb + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0);
+    load_blk(b0, kb + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1);
+    load_blk(b1, kb + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b2);
   }
+  // 0-2 blocks left, already in b0 (and b1)
+  if (kb < nkb) compute(b0);
+  if (kb + 1 < nkb) compute(b1);
 
 #pragma unroll
   for (int t = 0; t < TG; ++t)
