@@ -276,8 +276,11 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
 // MODE 0: gate/up (A = gathered x), h stored as bf16; MODE 1: down (A = bf16 h).
 constexpr uint32_t kMinus136x2 = 0xC308C308u;  // bf16 -136 in both halves
 
+// Occupancy: three waves per SIMD for one token group of bf16 rows (what
+// decode batches use), which fits the three register sets in 168 registers.
 template <int MODE, bool XF32, int TG>
-__global__ __launch_bounds__(256) void stream_int4_kernel(GemmGeom g, const void* __restrict__ a_src,
+__global__ __launch_bounds__(256, XF32 ? 1 : (TG == 1 ? 3 : (TG == 2 ? 2 : 1)))
+void stream_int4_kernel(GemmGeom g, const void* __restrict__ a_src,
                                                           const int32_t* __restrict__ row_tok,
                                                           float* __restrict__ out, int hstride,
                                                           int nblk) {
