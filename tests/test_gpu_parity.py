@@ -223,6 +223,22 @@ def test_decode_ragged(tokens):
     _run(W["decode"], tokens=tokens, max_tokens=32)
 
 
+@pytest.mark.parametrize("tokens", [128, 257, 1025])
+def test_mid_size_batches_sampled(tokens):
+    """Batch sizes between decode and prefill at the full layer shape: 128
+    (2 token groups per tile), 257 (first size on the wide router kernel),
+    1025 (first size on the multi-workgroup dispatch, 4 token groups)."""
+    s = W["decode"].replace(name=f"mid_{tokens}", tokens=tokens)
+    _run(s, sample=_spread(tokens, 10))
+
+
+def test_int4_two_token_groups_sampled():
+    """INT4 weights with 2 token groups per tile (the INT4 kernels' other
+    register budget)."""
+    s = W["int4_decode"].replace(name="int4_256", tokens=256)
+    _run(s, sample=_spread(256, 10))
+
+
 # ----------------------------------------------------------------- further shapes from the pages
 
 STEP3 = W["decode"].replace(name="step3", hidden=7168, experts=48, top_k=3, inter=5120,
