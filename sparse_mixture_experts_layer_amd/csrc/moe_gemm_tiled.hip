@@ -46,9 +46,12 @@ typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
 constexpr int kLoadsPerStage = 6;             // per wave: 2 A + 4 B fragments
 
-// One wave-wide 16-byte-per-lane load into LDS at `lds` (+ 16 * lane).
+// One wave-wide 16-byte-per-lane load of (src + OFF) into LDS at lds + OFF
+// (+ 16 * lane); OFF is an immediate, applied by the instruction to both
+// addresses.
+template <int OFF>
 __device__ __forceinline__ void load_frag(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)lds, 16, OFF, 0);
 }
 
 // Workgroup barrier without a memory fence: __syncthreads' release fence
@@ -156,15 +159,21 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
                         (size_t)(bblk < nblocks ? bblk : 0) * nk * 4 * kFragBytes + lane * 16;
 
   const uint16_t* a_base = a_src;
+  // One LDS base per operand and stage; the fragments are told apart by the
+  // instruction's immediate offset, which the global->LDS load adds to both
+  // the global and the LDS address (two M0 writes per stage instead of six).
   auto issue = [&](int kk, int stage) {
     uint8_t* st = lds + stage * kStageBytes;
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-      load_frag(a_base + a_off[f] + (size_t)kk * 32, st + (2 * wave + f) * kFragBytes);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      load_frag(bsrc + (size_t)kk * 4 * kFragBytes + q * kFragBytes,
-                st + (kAFrags + 4 * wave + q) * kFragBytes);
+    uint8_t* la = st + 2 * wave * kFragBytes;
+    load_frag<0>(a_base + a_off[0] + (size_t)kk * 32, la);
+    load_frag<kFragBytes>(
+        reinterpret_cast<const uint8_t*>(a_base + a_off[1] + (size_t)kk * 32) - kFragBytes, la);
+    uint8_t* lb = st + (kAFrags + 4 * wave) * kFragBytes;
+    const uint8_t* gb = bsrc + (size_t)kk * 4 * kFragBytes;
+    load_frag<0>(gb, lb);
+    load_frag<kFragBytes>(gb, lb);
+    load_frag<2 * kFragBytes>(gb, lb);
+    load_frag<3 * kFragBytes>(gb, lb);
   };
   auto rd_a = [&](int stage, int m) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + stage * kStageBytes +
