@@ -114,7 +114,9 @@ Plan make_plan(const moe_layer& L, int T) {
   // MFMA-bound regime: LDS-staged 128-row tiles with bf16 h (bf16 weights and
   // activations only)
   p.tiled = rows_per_expert >= 64.0 && c.weight_dtype == MOE_BF16 && c.act_dtype == MOE_BF16;
-  if (p.tiled) p.tg = 8;
+  // 256-row tiles (one 8-wave workgroup per CU) once experts hold ~200+ rows:
+  // fewer bytes pulled per flop, the bound of these GEMMs
+  if (p.tiled) p.tg = rows_per_expert >= 192.0 ? 16 : 8;
   const int bm = 16 * p.tg;
   const int nz = c.num_experts < p.P ? c.num_experts : p.P;
   p.max_tiles = nz + p.P / bm + (p.has_shared ? (T + bm - 1) / bm : 0) + 1;

@@ -1,23 +1,25 @@
-// Grouped expert GEMMs for large batches (prefill): LDS-staged 128 x 256 tiles
-// on bf16 MFMA, the MFMA-bound regime where each expert sees hundreds of rows.
+// Grouped expert GEMMs for large batches (prefill): LDS-staged tiles on bf16
+// MFMA, the regime where each expert sees hundreds of rows.
 //   gate/up:  h[r][f] = bf16(silu(x_r . Wg[f]) * (x_r . Wu[f]))   (r gathered via row_tok)
 //   down:     Y[r][n] = h_r . Wd[n]                                (fp32)
 // Expert FFN shape: llm-atlas "Step-3.5-Flash", "Champs bruts du config.json"
 // (moe_intermediate_size, share_expert_dim, hidden_size); SiLU gating is the
 // reading taken for the swiglu fields.
 //
-// Workgroup: 4 waves, tile = 128 rows x 256 weight rows; wave (wm, wn) owns
-// rows 64*wm .. +63 and weight rows 128*wn .. +127 (4 x 8 fragments of
-// 16x16, 128 fp32 accumulators per lane).  K advances 32 per stage through a
-// 3-stage LDS ring (24 KiB per stage): each stage is 8 A fragments (token
+// Tile = TM rows x 256 weight rows, TM = 128 (4 waves, two workgroups per CU)
+// or 256 (8 waves, one workgroup per CU; for experts with a few hundred rows:
+// the CUs then pull a third fewer bytes per flop, which is what bounds these
+// GEMMs).  Wave (wm, wn) owns rows 64*wm .. +63 and weight rows 128*wn .. +127
+// (4 x 8 fragments of 16x16, 128 fp32 accumulators per lane).  K advances 32
+// per stage through a 3-stage LDS ring: each stage is TM/16 A fragments (token
 // rows, gathered straight from x by per-lane addresses) and 16 B fragments
-// (packed weights), each 1 KiB and each written by one wave-wide
-// global->LDS load in MFMA operand order, so every LDS read is a contiguous
-// 1 KiB ds_read_b128 with no bank conflicts and no register staging.
-// Two stages are in flight while the third is multiplied, and the fragments
-// of the next stage are read into registers during the current MFMAs.  Two
-// workgroups share a CU (one wave of each per SIMD), so one's LDS traffic and
-// barrier waits overlap the other's MFMAs.
+// (packed weights), each 1 KiB and each written by one wave-wide global->LDS
+// load in MFMA operand order, so every LDS read is a contiguous 1 KiB
+// ds_read_b128 with no bank conflicts and no register staging.  Two stages are
+// in flight while the third is multiplied, and the fragments of the next
+// stage are read into registers during the current MFMAs.  Every SIMD runs two
+// waves (of two workgroups, or of one 8-wave workgroup), so one's LDS traffic
+// and barrier waits overlap the other's MFMAs.
 //
 // Precision: routed rows keep h in bf16 (one rounding, what the MFMA takes).
 // The shared expert enters the output unweighted, so its rounding error would
@@ -32,19 +34,28 @@
 namespace moe {
 namespace {
 
-constexpr int kTM = 128;                      // rows per tile
 constexpr int kTN = 256;                      // weight rows per tile
 constexpr int kStages = 3;
-constexpr int kAFrags = kTM / 16;             // 8
 constexpr int kBFrags = kTN / 16;             // 16
-constexpr int kStageBytes = (kAFrags + kBFrags) * kFragBytes;  // 24 KiB
 constexpr int kXcds = 8;
-static_assert(4 * 32 * (128 * 4 + 16) <= kStages * kStageBytes, "Y staging fits the ring");
+
+// Per tile height TM: waves, fragments per stage, loads per wave and stage.
+template <int TM>
+struct TileShape {
+  static constexpr int kWaves = TM / 32;                          // 4 or 8
+  static constexpr int kAFrags = TM / 16;                         // 8 or 16
+  static constexpr int kStageBytes = (kAFrags + kBFrags) * kFragBytes;
+  static constexpr int kAL = kAFrags / kWaves;                    // 2
+  static constexpr int kBL = kBFrags / kWaves;                    // 4 or 2
+  static constexpr int kLoads = kAL + kBL;                        // 6 or 4
+  // Y staging in the epilogue: MP fragment rows (16 rows each) per pass
+  static constexpr int kMP = TM == 128 ? 2 : 1;
+  static constexpr int kPitch = 128 * 4 + 16;                     // bytes per staged row
+  static_assert(kWaves * kMP * 16 * kPitch <= kStages * kStageBytes, "Y staging fits the ring");
+};
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
-
-constexpr int kLoadsPerStage = 6;             // per wave: 2 A + 4 B fragments
 
 // One wave-wide 16-byte-per-lane load of (src + OFF) into LDS at lds + OFF
 // (+ 16 * lane); OFF is an immediate, applied by the instruction to both
@@ -70,17 +81,22 @@ __device__ __forceinline__ void barrier() {
 __device__ __forceinline__ void wait_vm_lgkm0(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
     case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
     case 12: __builtin_amdgcn_s_waitcnt(0x007C); break;
     default: __builtin_amdgcn_s_waitcnt(0x0070); break;  // stricter than asked: always safe
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_t* __restrict__ a_src,
+template <int MODE, int TM>
+__global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGeom g, const uint16_t* __restrict__ a_src,
                                                     const int32_t* __restrict__ row_tok,
                                                     void* __restrict__ out, int hstride,
                                                     uint16_t* __restrict__ h_lo, int nblk) {
+  using TS = TileShape<TM>;
+  constexpr int kAFrags = TS::kAFrags, kStageBytes = TS::kStageBytes;
+  constexpr int kAL = TS::kAL, kBL = TS::kBL, kLoadsPerStage = TS::kLoads;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
   // Work order.  Workgroups are dealt round-robin over the 8 XCDs (each with
@@ -108,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
   int nb, mt;
   if (MODE == 0) {
     const int first = w / nblk - tile_m(v0);
-    const int ntg = (g.counts[group] + kTM - 1) / kTM;
+    const int ntg = (g.counts[group] + TM - 1) / TM;
     const int local = w - first * nblk;
     nb = local / ntg;
     mt = local % ntg;
@@ -116,8 +132,8 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
     nb = w % nblk;
     mt = tile_m(v0);
   }
-  const int row0 = g.offsets[group] + mt * kTM;
-  const int nrows = min(kTM, g.counts[group] - mt * kTM);
+  const int row0 = g.offsets[group] + mt * TM;
+  const int nrows = min(TM, g.counts[group] - mt * TM);
   if (nrows <= 0) return;
   const int width = group == g.E ? g.Is : g.I;
   const int H = g.H;
@@ -131,6 +147,7 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
 
   // this wave's two A fragments (rows 16*(2*wave) .. +31 of the tile); for the
   // shared group's down GEMM, pass 1 reads the lo plane (row - shared_base)
+  static_assert(kAL == 2, "two A fragments per wave and stage");
   const bool shared = group == g.E;
   const int shared_base = g.offsets[g.E];
   const int npass = (MODE == 1 && shared) ? 2 : 1;
@@ -150,13 +167,16 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
       }
     }
   };
-  // this wave's B block (4 fragments, 4 KiB per k-step).  A wave past the
-  // last block loads block 0 instead (its columns are never stored), so every
-  // wave issues the same number of loads per stage.
-  const int bblk = nb * 4 + wave;
+  // this wave's kBL B fragments: fragments kBL*wave .. of the tile's 16, i.e.
+  // fragments (kBL*wave) % 4 .. of 64-row weight block nb*4 + kBL*wave/4
+  // (each block is 4 KiB per k-step, its fragments contiguous).  A wave past
+  // the last block loads block 0 instead (its columns are never stored), so
+  // every wave issues the same number of loads per stage.
+  const int bblk = nb * 4 + kBL * wave / 4;
   const uint8_t* bsrc = g.packed + (size_t)group * g.expert_bytes +
                         (MODE == 0 ? 0 : (size_t)2 * width * H * 2) +
-                        (size_t)(bblk < nblocks ? bblk : 0) * nk * 4 * kFragBytes + lane * 16;
+                        (size_t)(bblk < nblocks ? bblk : 0) * nk * 4 * kFragBytes +
+                        (kBL * wave % 4) * kFragBytes + lane * 16;
 
   const uint16_t* a_base = a_src;
   // One LDS base per operand and stage; the fragments are told apart by the
@@ -168,12 +188,14 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
     load_frag<0>(a_base + a_off[0] + (size_t)kk * 32, la);
     load_frag<kFragBytes>(
         reinterpret_cast<const uint8_t*>(a_base + a_off[1] + (size_t)kk * 32) - kFragBytes, la);
-    uint8_t* lb = st + (kAFrags + 4 * wave) * kFragBytes;
+    uint8_t* lb = st + (kAFrags + kBL * wave) * kFragBytes;
     const uint8_t* gb = bsrc + (size_t)kk * 4 * kFragBytes;
     load_frag<0>(gb, lb);
     load_frag<kFragBytes>(gb, lb);
-    load_frag<2 * kFragBytes>(gb, lb);
-    load_frag<3 * kFragBytes>(gb, lb);
+    if (kBL == 4) {
+      load_frag<2 * kFragBytes>(gb, lb);
+      load_frag<3 * kFragBytes>(gb, lb);
+    }
   };
   auto rd_a = [&](int stage, int m) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + stage * kStageBytes +
@@ -245,27 +267,29 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
     // a wave writes whole 512-byte row segments (direct stores from the MFMA
     // layout would write 64-byte pieces, 4 bytes per lane).  The ring is idle:
     // every wave passed the last k-step's barrier after its last LDS read.
-    // Each wave stages its 64 x 128 block in two halves of 32 rows in a
-    // private region; rows are padded by 16 bytes against bank conflicts.
-    constexpr int kPitch = 128 * 4 + 16;
-    uint8_t* stg = lds + wave * (32 * kPitch);
+    // Each wave stages its 64 x 128 block kMP fragment rows (16 rows each) at
+    // a time in a private region; rows are padded by 16 bytes against bank
+    // conflicts.
+    constexpr int kMP = TS::kMP, kPitch = TS::kPitch;
+    uint8_t* stg = lds + wave * (kMP * 16 * kPitch);
     const int blk0 = nb * 4 + wn * 2;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int pass = 0; pass < 4 / kMP; ++pass) {
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
+      for (int mm = 0; mm < kMP; ++mm)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int lr = mm * 16 + (lane >> 4) * 4 + i, lc = j * 16 + (lane & 15);
-            *reinterpret_cast<float*>(stg + lr * kPitch + lc * 4) = acc[2 * half + mm][j][i];
+            *reinterpret_cast<float*>(stg + lr * kPitch + lc * 4) = acc[kMP * pass + mm][j][i];
           }
+      // kMP*16 rows x 32 chunks of 16 bytes, 64 chunks per wave-wide step
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < kMP * 8; ++q) {
         const int idx = q * kWave + lane, lr = idx >> 5, ch = idx & 31;
         const f32x4 val = *reinterpret_cast<const f32x4*>(stg + lr * kPitch + ch * 16);
-        const int r = wm * 64 + half * 32 + lr;
+        const int r = wm * 64 + pass * kMP * 16 + lr;
         const int blk = blk0 + (ch >> 4);
         if (r < nrows && blk < nblocks)
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)(row0 + r) * H +
@@ -303,23 +327,34 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(GemmGeom g, const uint16_
 
 hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32_t* row_tok,
                                uint16_t* h, uint16_t* h_lo, int hstride, hipStream_t s) {
-  if (16 * g.tg != kTM) return hipErrorInvalidValue;
+  const int tm = 16 * g.tg;
+  if (tm != 128 && tm != 256) return hipErrorInvalidValue;
   const int wmax = g.I > g.Is ? g.I : g.Is;
   const int nblk = (2 * wmax + kTN - 1) / kTN;
   const size_t items = (size_t)g.max_tiles * nblk;
-  dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(256);
-  hipLaunchKernelGGL((tiled_kernel<0>), grid, block, 0, s, g, x, row_tok, h, hstride, h_lo, nblk);
+  dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(2 * tm);
+  if (tm == 256)
+    hipLaunchKernelGGL((tiled_kernel<0, 256>), grid, block, 0, s, g, x, row_tok, h, hstride, h_lo,
+                       nblk);
+  else
+    hipLaunchKernelGGL((tiled_kernel<0, 128>), grid, block, 0, s, g, x, row_tok, h, hstride, h_lo,
+                       nblk);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_t* h_lo,
                              int hstride, float* y, hipStream_t s) {
-  if (16 * g.tg != kTM) return hipErrorInvalidValue;
+  const int tm = 16 * g.tg;
+  if (tm != 128 && tm != 256) return hipErrorInvalidValue;
   const int nblk = (g.H + kTN - 1) / kTN;
   const size_t items = (size_t)g.max_tiles * nblk;
-  dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(256);
-  hipLaunchKernelGGL((tiled_kernel<1>), grid, block, 0, s, g, h, nullptr, y, hstride,
-                     const_cast<uint16_t*>(h_lo), nblk);
+  dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(2 * tm);
+  if (tm == 256)
+    hipLaunchKernelGGL((tiled_kernel<1, 256>), grid, block, 0, s, g, h, nullptr, y, hstride,
+                       const_cast<uint16_t*>(h_lo), nblk);
+  else
+    hipLaunchKernelGGL((tiled_kernel<1, 128>), grid, block, 0, s, g, h, nullptr, y, hstride,
+                       const_cast<uint16_t*>(h_lo), nblk);
   return hipGetLastError();
 }
 
