@@ -100,16 +100,16 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
   // Work order.  Workgroups are dealt round-robin over the 8 XCDs (each with
-  // its own L2; all share the last-level cache).
+  // its own L2; all share the last-level cache).  Inside an expert the
+  // m-tiles are the fastest index (except for 128-row down tiles), so the
+  // workgroups streaming one weight block start together.
   //   gate/up: the work list is cut into 8 contiguous chunks, one per XCD, so
-  //     each XCD runs whole experts; inside an expert the m-tiles are the
-  //     fastest index, so the workgroups streaming one weight block start
-  //     together and share it through L2 (the gathered x rows they also need
-  //     stay in the last-level cache).
-  //   down: plain round-robin with weight blocks fastest, so the 8 XCDs work
-  //     on the same expert at once: its weights are fetched from HBM once
-  //     into the last-level cache, and each XCD keeps only 2 of the 16 weight
-  //     blocks of an expert plus the h tiles in its L2.
+  //     each XCD runs whole experts and its m-tiles share the weight blocks
+  //     through L2 (the gathered x rows they also need stay in the
+  //     last-level cache);
+  //   down: plain round-robin, so the 8 XCDs work on the same expert at once:
+  //     its weights are fetched from HBM once into the last-level cache and
+  //     each XCD keeps a slice of them and the h tiles in its L2.
   const int total = *g.ntiles * nblk;
   int w = (int)blockIdx.x;
   if (MODE == 0) {
@@ -122,13 +122,13 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   const int v0 = g.tiles[w / nblk];
   const int group = tile_group(v0);
   int nb, mt;
-  if (MODE == 0) {
+  if (MODE == 0 || TM == 256) {  // m-tiles fastest inside the group
     const int first = w / nblk - tile_m(v0);
     const int ntg = (g.counts[group] + TM - 1) / TM;
     const int local = w - first * nblk;
     nb = local / ntg;
     mt = local % ntg;
-  } else {
+  } else {                       // weight blocks fastest (measured better here)
     nb = w % nblk;
     mt = tile_m(v0);
   }
