@@ -85,6 +85,8 @@ __device__ __forceinline__ void wait_vm_lgkm0(int n) {
     case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
     case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
     case 12: __builtin_amdgcn_s_waitcnt(0x007C); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4070); break;
+    case 18: __builtin_amdgcn_s_waitcnt(0x4072); break;
     default: __builtin_amdgcn_s_waitcnt(0x0070); break;  // stricter than asked: always safe
   }
 }
@@ -235,7 +237,13 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     }
   };
   // loads issued after stage kk+1 that may still be in flight at step kk
-  auto vm_at = [&](int kk) { return kk + 2 < nk ? kLoadsPerStage : 0; };
+  // (stages kk+2 .. kk+kStages-1 that exist)
+  auto vm_at = [&](int kk) {
+    int n = nk - kk - 2;
+    n = n < 0 ? 0 : (n > kStages - 2 ? kStages - 2 : n);
+    return n * kLoadsPerStage;
+  };
+  constexpr int kVmMain = (kStages - 2) * kLoadsPerStage;
 
   for (int pass = 0; pass < npass; ++pass) {
     // pass 1 (shared group, down GEMM) starts after the last step's barrier
@@ -252,8 +260,8 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     for (int j = 0; j < 8; ++j) b[j] = rd_b(0, j);
     int kk = 0;
     for (; kk + kStages + 1 < nk; kk += 2) {
-      step(kk, a0, a1, true, true, kLoadsPerStage);
-      step(kk + 1, a1, a0, true, true, kLoadsPerStage);
+      step(kk, a0, a1, true, true, kVmMain);
+      step(kk + 1, a1, a0, true, true, kVmMain);
     }
     for (; kk < nk; kk += 2) {
       step(kk, a0, a1, kk + kStages < nk, kk + 1 < nk, vm_at(kk));
