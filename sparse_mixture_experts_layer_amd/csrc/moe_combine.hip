@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __syncthreads();
   // Each thread owns kChunks column groups of 4 per pass, so every row's
   // loads for all of them are in flight together (bandwidth-bound kernel).
+  // Y is read once: nontemporal loads keep it from displacing cached data.
   constexpr int kChunks = 4;
   const int stride = blockDim.x * 4;
   for (int c0 = 0; c0 < H; c0 += stride * kChunks) {
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       col[i] = c0 + i * stride + threadIdx.x * 4;
       acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (has_shared && col[i] < H)
-        acc[i] = *reinterpret_cast<const f32x4*>(y + (size_t)(P + t) * H + col[i]);
+        acc[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)(P + t) * H + col[i]));
     }
     for (int j = 0; j < k; ++j) {
       const float* yr = y + (size_t)rows[j] * H;
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       f32x4 v[kChunks];
 #pragma unroll
       for (int i = 0; i < kChunks; ++i)
-        v[i] = col[i] < H ? *reinterpret_cast<const f32x4*>(yr + col[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[i] = col[i] < H ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yr + col[i])) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < kChunks; ++i)
 #pragma unroll

@@ -299,9 +299,10 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         const f32x4 val = *reinterpret_cast<const f32x4*>(stg + lr * kPitch + ch * 16);
         const int r = wm * 64 + pass * kMP * 16 + lr;
         const int blk = blk0 + (ch >> 4);
-        if (r < nrows && blk < nblocks)
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)(row0 + r) * H +
-                                    blk * 64 + (ch & 15) * 4) = val;
+        if (r < nrows && blk < nblocks)  // read once, by combine: nontemporal
+          __builtin_nontemporal_store(
+              val, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)(row0 + r) * H +
+                                            blk * 64 + (ch & 15) * 4));
       }
     }
     return;
