@@ -111,8 +111,8 @@ Plan make_plan(const moe_layer& L, int T) {
   const double rows_per_expert = (double)p.P / c.num_experts;
   p.tg = rows_per_expert < 2.0 ? 1 : (rows_per_expert < 24.0 ? 2 : 4);
   if (c.weight_dtype == MOE_INT4_G32 && p.tg > 2) p.tg = 2;  // register budget
-  // MFMA-bound regime: LDS-staged 128-row tiles with bf16 h (bf16 weights and
-  // activations only)
+  // MFMA regime (64+ rows per expert): LDS-staged tiles with bf16 h (bf16
+  // weights and activations only)
   p.tiled = rows_per_expert >= 64.0 && c.weight_dtype == MOE_BF16 && c.act_dtype == MOE_BF16;
   // 256-row tiles (one 8-wave workgroup per CU) once experts hold ~200+ rows:
   // fewer bytes pulled per flop, the bound of these GEMMs

@@ -55,8 +55,9 @@ hipError_t launch_gateup(const GemmGeom& g, bool int4, bool act_f32, const void*
 hipError_t launch_down(const GemmGeom& g, bool int4, bool act_f32, const void* h,
                        const uint16_t* h_lo, int hstride, float* y, hipStream_t s);
 
-// Large-batch (MFMA-bound) variants: 128-row tiles (g.tg must be 8), bf16 h;
-// the shared group's h also gets a bf16 remainder plane h_lo ([T][hstride]).
+// Large-batch variants: LDS-staged tiles of 128 or 256 rows (g.tg 8 or 16,
+// any other value is rejected), bf16 h; the shared group's h also gets a bf16
+// remainder plane h_lo ([T][hstride]).
 hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32_t* row_tok,
                                uint16_t* h, uint16_t* h_lo, int hstride, hipStream_t s);
 hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_t* h_lo,
