@@ -30,7 +30,9 @@ design notes):
 * Expert FFN: SiLU-gated (gate -> SiLU, up -> linear, h = silu(gate) * up,
   y = down h).  Three matrices per expert are implied by the 196B total
   parameter count; gating is implied by the swiglu_limits fields, whose value
-  is 0 (no clamp) for every MoE layer.
+  is 0 (no clamp) for every MoE layer.  A nonzero limit L (7 for the routed
+  and 16 for the shared experts of the last layers) is read as clamping the
+  gate projection to at most L and the up projection to [-L, L].
 * No bias terms in the expert linears; the shared expert is added unweighted.
 * Router bias: added to the logits before selection and weighting
   (bias_mode="logit"); bias_mode="select" uses it for selection only.
@@ -43,7 +45,8 @@ Parity pins (tests/test_oracle_pins.py): brute-force full-sort top-k, the
 closed-form renormalised weights, k = 1 and k = E special cases, identical
 experts reducing to a dense SwiGLU FFN, a hand-computed two-expert case
 (tests/golden/hand_two_expert.json), expert-relabelling and token-independence
-invariants, INT4 dequantisation bounds, and dispatch against a Python sort.
+invariants, INT4 dequantisation bounds, dispatch against a Python sort, and
+hand-evaluated SwiGLU limits.
 """
 from __future__ import annotations
 
@@ -137,11 +140,21 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def swiglu_ffn(x_rows: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
-               w_down: np.ndarray) -> np.ndarray:
-    """y = W_down (silu(W_gate x) * (W_up x)) for each row of x_rows (float64)."""
+               w_down: np.ndarray, limit: float = 0.0) -> np.ndarray:
+    """y = W_down (silu(g) * u), g = W_gate x, u = W_up x, for each row of x_rows
+    (float64).
+
+    limit > 0 bounds the two projections before the product: g to at most
+    limit, u to [-limit, limit].  Source: llm-atlas "Step-3.5-Flash", config
+    fields swiglu_limits (0 on every layer but the last two, 7 there) and
+    swiglu_limits_shared (16 on the last layer, for the shared expert).  The
+    pages give only the values; this clamp form is the reading taken."""
     x_rows = np.asarray(x_rows, np.float64)
     g = x_rows @ np.asarray(w_gate, np.float64).T
     u = x_rows @ np.asarray(w_up, np.float64).T
+    if limit > 0:
+        g = np.minimum(g, limit)
+        u = np.clip(u, -limit, limit)
     return (silu(g) * u) @ np.asarray(w_down, np.float64).T
 
 
@@ -163,13 +176,16 @@ def dequant_int4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 def forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
             experts: Callable[[int], Expert], shared: Optional[Expert], top_k: int,
             score: str = "softmax", renormalize: bool = True, routed_scale: float = 1.0,
-            bias_mode: str = "logit", force_idx: Optional[np.ndarray] = None):
+            bias_mode: str = "logit", force_idx: Optional[np.ndarray] = None,
+            swiglu_limit: float = 0.0, swiglu_limit_shared: float = 0.0):
     """The whole layer on the host.  Returns (y [T][H] float64, idx, w, logits32).
 
     experts(e) returns that expert's (W_gate, W_up, W_down); it is called once
     per expert that at least one token selected, so large layers can be
     materialised one expert at a time.  force_idx, if given, replaces the
-    selection (the weights are still computed from the logits)."""
+    selection (the weights are still computed from the logits).
+    swiglu_limit / swiglu_limit_shared: the routed / shared experts' SwiGLU
+    limits (0 = none; see swiglu_ffn)."""
     x = np.asarray(x, np.float64)
     t = x.shape[0]
     idx, w, l32 = route(x, w_router, bias, top_k, score, renormalize, routed_scale, bias_mode)
@@ -178,10 +194,10 @@ def forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
         w = gate_weights(l32, idx, score, renormalize, routed_scale)
     y = np.zeros((t, x.shape[1]), np.float64)
     if shared is not None:
-        y += swiglu_ffn(x, *shared)
+        y += swiglu_ffn(x, *shared, limit=swiglu_limit_shared)
     for e in np.unique(idx):
         tok, slot = np.nonzero(idx == e)
-        y_e = swiglu_ffn(x[tok], *experts(int(e)))
+        y_e = swiglu_ffn(x[tok], *experts(int(e)), limit=swiglu_limit)
         y[tok] += w[tok, slot][:, None] * y_e
     return y, idx, w, l32
 

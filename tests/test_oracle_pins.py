@@ -235,10 +235,34 @@ def check_parameter_count():
     assert abs(active / 1e9 - 11) < 0.5
 
 
+def check_swiglu_limit():
+    """SwiGLU limits by hand: gate clamped from above only, up on both sides;
+    routed and shared experts each take their own limit."""
+    silu = lambda z: z / (1.0 + math.exp(-z))
+    x = np.array([[1.0]])
+    wd = np.array([[1.0]])
+    # gate 10 > 7 -> 7, up -20 < -7 -> -7
+    y = oracle.swiglu_ffn(x, np.array([[10.0]]), np.array([[-20.0]]), wd, limit=7.0)
+    assert y[0, 0] == pytest.approx(silu(7.0) * -7.0, rel=1e-14)
+    # gate -10 is not clamped from below; up 5 inside the limit
+    y = oracle.swiglu_ffn(x, np.array([[-10.0]]), np.array([[5.0]]), wd, limit=7.0)
+    assert y[0, 0] == pytest.approx(silu(-10.0) * 5.0, rel=1e-14)
+    # no limit: untouched
+    y = oracle.swiglu_ffn(x, np.array([[10.0]]), np.array([[-20.0]]), wd)
+    assert y[0, 0] == pytest.approx(silu(10.0) * -20.0, rel=1e-14)
+    # whole layer, one token, one expert (weight 1): routed limit 7, shared 16,
+    # both projections at 10 -> routed clamped to (7, 7), shared untouched
+    ex = (np.array([[10.0]]), np.array([[10.0]]), np.array([[1.0]]))
+    y, idx, w, _ = oracle.forward(x, np.array([[1.0]]), None, lambda e: ex, ex, 1,
+                                  swiglu_limit=7.0, swiglu_limit_shared=16.0)
+    assert w[0, 0] == 1.0
+    assert y[0, 0] == pytest.approx(silu(10.0) * 10.0 + silu(7.0) * 7.0, rel=1e-14)
+
+
 PINS = [check_hand_case, check_topk_bruteforce, check_weights_closed_form,
         check_identical_experts_dense, check_single_expert_contribution,
         check_relabel_and_token_independence, check_router_bias_and_fp32_logits,
-        check_dispatch, check_int4, check_parameter_count]
+        check_dispatch, check_int4, check_parameter_count, check_swiglu_limit]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -250,7 +274,7 @@ def test_pin(pin):
 
 def _mut_swap_gate_up(m):
     orig = m.swiglu_ffn
-    m.swiglu_ffn = lambda x, g, u, d: orig(x, u, g, d)
+    m.swiglu_ffn = lambda x, g, u, d, limit=0.0: orig(x, u, g, d, limit)
 
 
 def _mut_no_renorm(m):
@@ -271,7 +295,7 @@ def _mut_silu_sign(m):
 
 
 def _mut_down_transposed(m):
-    def ffn(x, g, u, d):
+    def ffn(x, g, u, d, limit=0.0):
         x = np.asarray(x, np.float64)
         h = m.silu(x @ g.T) * (x @ u.T)
         return h @ np.asarray(d).reshape(d.shape[1], d.shape[0])
@@ -315,9 +339,28 @@ def _mut_dispatch_unstable(m):
     m.dispatch = disp
 
 
+def _mut_limit_gate_only(m):
+    def ffn(x, g, u, d, limit=0.0):
+        x = np.asarray(x, np.float64)
+        gg = x @ np.asarray(g, np.float64).T
+        if limit > 0:
+            gg = np.minimum(gg, limit)
+        return (m.silu(gg) * (x @ np.asarray(u, np.float64).T)) @ np.asarray(d, np.float64).T
+    m.swiglu_ffn = ffn
+
+
+def _mut_limit_shared_uses_routed(m):
+    orig = m.forward
+
+    def fwd(*a, swiglu_limit=0.0, swiglu_limit_shared=0.0, **kw):
+        return orig(*a, swiglu_limit=swiglu_limit, swiglu_limit_shared=swiglu_limit, **kw)
+    m.forward = fwd
+
+
 MUTATIONS = [_mut_swap_gate_up, _mut_no_renorm, _mut_tie_high_index, _mut_silu_sign,
              _mut_down_transposed, _mut_softmax_no_max_shift_wrong, _mut_shared_weighted,
-             _mut_int4_high_nibble_first, _mut_dispatch_unstable]
+             _mut_int4_high_nibble_first, _mut_dispatch_unstable, _mut_limit_gate_only,
+             _mut_limit_shared_uses_routed]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
