@@ -12,7 +12,8 @@ on its own stream during those same K steps.  Prints one JSON line.
 Workloads (seeded synthetic inputs, shapes from the llm-atlas "Step-3.5-Flash"
 config fields): decode (32 tokens, default), verify (256 tokens, Zipf expert
 popularity), prefill (16384 tokens), int4_decode (32 tokens, INT4-g32 weights),
-tiny (parity-sized).
+mtp_decode (32 tokens through a last layer: SwiGLU limits 7 routed / 16 shared,
+activations drawn 8x wider so that the limits act), tiny (parity-sized).
 """
 from __future__ import annotations
 
@@ -47,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "verify", "prefill", "int4_decode"])
+                    choices=["tiny", "decode", "verify", "prefill", "int4_decode", "mtp_decode"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle on the host (e.g. under a profiler)")
@@ -130,7 +131,8 @@ def cpu_baseline(inp, shape, target_s: float):
         for e in np.unique(idx):
             fetch(int(e))
         t0 = time.perf_counter()
-        oracle.forward(x64[:s], wr, bias, experts, shared, shape.top_k)
+        oracle.forward(x64[:s], wr, bias, experts, shared, shape.top_k,
+                       swiglu_limit=shape.swiglu_limit, swiglu_limit_shared=shape.swiglu_limit_shared)
         elapsed = time.perf_counter() - t0
         if elapsed >= target_s or s >= T:
             break
@@ -231,7 +233,8 @@ def main():
     wl_desc = {"tiny": "tiny parity layer", "decode": "Step-3.5-Flash MoE layer, decode batch",
                "verify": "Step-3.5-Flash MoE layer, MTP verify batch (64 streams x 4), Zipf experts",
                "prefill": "Step-3.5-Flash MoE layer, prefill chunk",
-               "int4_decode": "Step-3.5-Flash MoE layer, decode batch, INT4-g32 weights"}
+               "int4_decode": "Step-3.5-Flash MoE layer, decode batch, INT4-g32 weights",
+               "mtp_decode": "Step-3.5-Flash last MoE layer (SwiGLU limits 7 / 16), decode batch"}
     line = {
         "metric": METRIC,
         "value": round(T / t_layer, 1),
@@ -244,11 +247,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if not int4 else "bf16 x int4-g32",
-        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "data": (f"synthetic (seeded N(0,{shape.x_scale:g}^2) activations, N(0,1/fan_in) weights)"
+                 if shape.x_scale != 1.0 else
+                 "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)"),
         "config": {"workload": f"{args.workload}: {wl_desc[args.workload]}", "tokens": T,
                    "hidden": H, "experts": E, "top_k": k, "expert_inter": I,
                    "shared_inter": Is, "weights": shape.weight_dtype,
-                   "routing": shape.routing, "parallelism": "single GPU"},
+                   "routing": shape.routing, "parallelism": "single GPU",
+                   **({"swiglu_limits": [shape.swiglu_limit, shape.swiglu_limit_shared]}
+                      if shape.swiglu_limit or shape.swiglu_limit_shared else {})},
         "roofline": roof,
         "layer": {**layer_frac, "alg_bytes": int(b_alg), "alg_flops": int(f_alg),
                   "experts_touched": U,

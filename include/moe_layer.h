@@ -13,7 +13,8 @@
  *     local-deployment paragraph: INT4-quantised weights for llama.cpp).
  *
  * y[t] = shared(x[t]) + sum_j w[t,j] * expert_{idx[t,j]}(x[t]),
- *   expert(x) = W_down (silu(W_gate x) * (W_up x)),  silu(z) = z / (1 + exp(-z)).
+ *   expert(x) = W_down (silu(W_gate x) * (W_up x)),  silu(z) = z / (1 + exp(-z))
+ *   (the two projections optionally clamped first: see the SwiGLU limits).
  * Router: l = x W_r^T (+ b), accumulated in fp32.  Experts are ranked by
  * descending l (ties: lower expert index).  softmax scoring:
  * p = softmax over all E; sigmoid scoring: p = 1/(1+exp(-l)).  With renormalize,
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_PACK_VERSION 1
 
 typedef struct moe_layer* moe_layer_t;
@@ -71,7 +72,13 @@ typedef enum { MOE_BIAS_LOGIT = 0, MOE_BIAS_SELECT = 1 } moe_bias_mode_t;
 /* Layer shape and numerics.  Limits: 1 <= top_k <= min(num_experts, 16),
  * num_experts <= 512, hidden % 64 == 0, inter % 32 == 0, shared_inter % 32 == 0
  * (0 = no shared expert), max_tokens >= 1.  INT4 weights additionally need
- * hidden, inter and shared_inter to be multiples of 128. */
+ * hidden, inter and shared_inter to be multiples of 128.
+ * SwiGLU limits (llm-atlas "Step-3.5-Flash", config fields swiglu_limits and
+ * swiglu_limits_shared: 0 on all layers but the last ones, where the routed
+ * experts take 7 and the shared expert 16): a limit L > 0 replaces the gate
+ * projection g by min(g, L) and the up projection u by min(max(u, -L), L)
+ * before silu(g) * u.  The pages give only the values; this clamp is the
+ * reading taken.  Each limit must be finite and >= 0 (MOE_ERR_SHAPE). */
 typedef struct {
   int32_t hidden;        /* H (hidden_size) */
   int32_t num_experts;   /* E (moe_num_experts) */
@@ -85,6 +92,8 @@ typedef struct {
   int32_t bias_mode;     /* moe_bias_mode_t; used only when a router bias is passed */
   int32_t act_dtype;     /* MOE_BF16 or MOE_F32: dtype of x and of the output */
   int32_t weight_dtype;  /* MOE_BF16 or MOE_INT4_G32: routed and shared expert weights */
+  float swiglu_limit;        /* routed experts' SwiGLU limit L (0 = none), see below */
+  float swiglu_limit_shared; /* the shared expert's SwiGLU limit (0 = none) */
 } moe_layer_config_t;
 
 /* Canonical (unpacked) expert weights, device pointers, read by

@@ -47,6 +47,9 @@ class LayerShape:
     routing: str = "uniform"       # "uniform" (no bias) | "zipf" (per-expert logit bias)
     renormalize: bool = True
     index: int = 0                 # workload index, part of every seed
+    x_scale: float = 1.0           # activations drawn from N(0, x_scale^2)
+    swiglu_limit: float = 0.0      # routed experts' SwiGLU limit (0 = none)
+    swiglu_limit_shared: float = 0.0  # shared expert's SwiGLU limit (0 = none)
 
     @property
     def pairs(self) -> int:
@@ -61,16 +64,24 @@ class LayerShape:
 
 STEP35 = dict(hidden=4096, experts=288, top_k=8, inter=1280, shared_inter=1280)
 
-# The five workloads.  Index 0 is the tiny case the oracle finishes in
+# The workloads.  Index 0 is the tiny case the oracle finishes in
 # milliseconds; 1 is single-stream-batch decode; 2 is a multi-token-prediction
 # verify batch (64 streams x (1+3) tokens) with Zipf expert popularity; 3 is a
-# prefill chunk; 4 is decode with INT4 group-32 weights.
+# prefill chunk; 4 is decode with INT4 group-32 weights; 5 is decode through
+# one of the last layers, whose SwiGLU limits are 7 (routed) and 16 (shared)
+# (llm-atlas "Step-3.5-Flash", config fields swiglu_limits and
+# swiglu_limits_shared), with activations drawn 8x wider so that the clamps
+# act: the projections then have a standard deviation near 8, and about a
+# third of the routed up values and a twentieth of the shared ones lie beyond
+# their limit.
 WORKLOADS = {
     "tiny": LayerShape("tiny", 64, 256, 16, 2, 64, 64, act_dtype="f32", index=0),
     "decode": LayerShape("decode", 32, **STEP35, index=1),
     "verify": LayerShape("verify", 256, **STEP35, routing="zipf", index=2),
     "prefill": LayerShape("prefill", 16384, **STEP35, index=3),
     "int4_decode": LayerShape("int4_decode", 32, **STEP35, weight_dtype="int4_g32", index=4),
+    "mtp_decode": LayerShape("mtp_decode", 32, **STEP35, x_scale=8.0, swiglu_limit=7.0,
+                             swiglu_limit_shared=16.0, index=5),
 }
 
 # tensor ids (part of the seed)
@@ -165,7 +176,7 @@ def make_layer(shape: LayerShape, seed: int = 0, device="cpu",
     T = shape.tokens if tokens is None else tokens
     H, E, I, Is = shape.hidden, shape.experts, shape.inter, shape.shared_inter
     act = torch.float32 if shape.act_dtype == "f32" else torch.bfloat16
-    x = _normal((T, H), 1.0, dev, seed_for(seed, wl, T_X), act)
+    x = _normal((T, H), shape.x_scale, dev, seed_for(seed, wl, T_X), act)
     router_w = _normal((E, H), 1.0 / math.sqrt(H), dev, seed_for(seed, wl, T_ROUTER), torch.bfloat16)
     bias = None
     if shape.routing == "zipf":

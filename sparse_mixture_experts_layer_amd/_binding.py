@@ -24,7 +24,8 @@ class MoeLayerConfig(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("num_experts", C.c_int32), ("top_k", C.c_int32),
                 ("inter", C.c_int32), ("shared_inter", C.c_int32), ("max_tokens", C.c_int32),
                 ("score", C.c_int32), ("renormalize", C.c_int32), ("routed_scale", C.c_float),
-                ("bias_mode", C.c_int32), ("act_dtype", C.c_int32), ("weight_dtype", C.c_int32)]
+                ("bias_mode", C.c_int32), ("act_dtype", C.c_int32), ("weight_dtype", C.c_int32),
+                ("swiglu_limit", C.c_float), ("swiglu_limit_shared", C.c_float)]
 
 
 class MoeWeights(C.Structure):

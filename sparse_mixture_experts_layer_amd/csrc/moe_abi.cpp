@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cfloat>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -68,6 +69,10 @@ moe_status_t check_config(const moe_layer_config_t* c) {
     return fail(MOE_ERR_DTYPE, "bias_mode must be MOE_BIAS_LOGIT or MOE_BIAS_SELECT");
   if (!(c->routed_scale == c->routed_scale) || c->routed_scale <= 0.f)
     return fail(MOE_ERR_SHAPE, "routed_scale must be a positive number");
+  if (!(c->swiglu_limit >= 0.f && c->swiglu_limit <= FLT_MAX) ||
+      !(c->swiglu_limit_shared >= 0.f && c->swiglu_limit_shared <= FLT_MAX))
+    return fail(MOE_ERR_SHAPE, "SwiGLU limits must be finite and >= 0 (got %g, %g)",
+                (double)c->swiglu_limit, (double)c->swiglu_limit_shared);
   if (c->num_experts < 1 || c->num_experts > 512)
     return fail(MOE_ERR_SHAPE, "num_experts must be in [1, 512] (got %d)", c->num_experts);
   if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->num_experts)
@@ -363,6 +368,8 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g.counts = counts;
   g.max_tiles = p.max_tiles;
   g.tg = p.tg;
+  g.limit = c.swiglu_limit;
+  g.limit_shared = c.swiglu_limit_shared;
   if (p.tiled) {
     uint16_t* hb = reinterpret_cast<uint16_t*>(h);
     uint16_t* hl = reinterpret_cast<uint16_t*>(ws + p.h_lo);

@@ -76,6 +76,17 @@ __device__ __forceinline__ void split_f32x8(const float* x, u32x4& hi, u32x4& lo
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// h = silu(g) * u; a limit lim > 0 first bounds g to at most lim and u to
+// [-lim, lim] (the SwiGLU limits of Step-3.5-Flash's last layers, 7 routed and
+// 16 shared); lim == 0 leaves both untouched.
+__device__ __forceinline__ float swiglu(float g, float u, float lim) {
+  if (lim > 0.f) {
+    g = fminf(g, lim);
+    u = fminf(fmaxf(u, -lim), lim);
+  }
+  return silu(g) * u;
+}
+
 // Expanding an INT4 dword (8 nibbles stored in the order k0,k2,k4,k6,k1,k3,k5,k7)
 // into 8 bf16 values 128 + u, u = q + 8 in [0, 15]: bf16 bits 0x4300 | u are
 // exactly 128 + u, so two masks and an OR per pair produce exact operands; the

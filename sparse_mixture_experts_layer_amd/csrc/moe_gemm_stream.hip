@@ -1,5 +1,6 @@
 // Grouped expert GEMMs that stream the packed weights once per tile:
 //   gate/up:  h[r][f] = silu(sum_k x[tok(r)][k] Wg[f][k]) * (sum_k x[tok(r)][k] Wu[f][k])
+//             (both sums first bounded by the group's SwiGLU limit, if any)
 //   down:     Y[r][n] = sum_f h[r][f] Wd[n][f]          (fp32 out)
 // for every permuted row r of every expert group (the shared expert is the
 // last group, over all tokens).  Expert FFN shape: llm-atlas "Step-3.5-Flash",
@@ -245,15 +246,18 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
       if (r >= ti.nrows) continue;
       const size_t row = (size_t)ti.row0 + r;
       if (MODE == 0 && HM == 0) {
+        const float lim = ti.group == g.E ? g.limit_shared : g.limit;
 #pragma unroll
         for (int f = 0; f < 2; ++f)
-          out[row * hstride + f0 + f * 16 + (lane & 15)] = silu(acc[t][f][i]) * acc[t][2 + f][i];
+          out[row * hstride + f0 + f * 16 + (lane & 15)] =
+              swiglu(acc[t][f][i], acc[t][2 + f][i], lim);
       } else if (MODE == 0) {
         uint16_t* hb = reinterpret_cast<uint16_t*>(out);
         const bool shared = ti.group == g.E;
+        const float lim = shared ? g.limit_shared : g.limit;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const float hv = silu(acc[t][f][i]) * acc[t][2 + f][i];
+          const float hv = swiglu(acc[t][f][i], acc[t][2 + f][i], lim);
           const uint16_t hi = f32_to_bf16_bits(hv);
           hb[row * hstride + f0 + f * 16 + (lane & 15)] = hi;
           if (shared)
@@ -411,10 +415,11 @@ void stream_int4_kernel(GemmGeom g, const void* __restrict__ a_src,
       const size_t row = (size_t)ti.row0 + r;
       if (MODE == 0) {
         uint16_t* hb = reinterpret_cast<uint16_t*>(out);
+        const float lim = ti.group == g.E ? g.limit_shared : g.limit;
 #pragma unroll
         for (int f = 0; f < 2; ++f)
           hb[row * hstride + f0 + f * 16 + (lane & 15)] =
-              f32_to_bf16_bits(silu(acc[t][f][i]) * acc[t][2 + f][i]);
+              f32_to_bf16_bits(swiglu(acc[t][f][i], acc[t][2 + f][i], lim));
       } else {
 #pragma unroll
         for (int f = 0; f < 4; ++f) out[row * H + f0 + f * 16 + (lane & 15)] = acc[t][f][i];

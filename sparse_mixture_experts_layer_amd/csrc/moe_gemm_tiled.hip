@@ -1,6 +1,7 @@
 // Grouped expert GEMMs for large batches (prefill): LDS-staged tiles on bf16
 // MFMA, the regime where each expert sees hundreds of rows.
-//   gate/up:  h[r][f] = bf16(silu(x_r . Wg[f]) * (x_r . Wu[f]))   (r gathered via row_tok)
+//   gate/up:  h[r][f] = bf16(silu(x_r . Wg[f]) * (x_r . Wu[f]))   (r gathered via row_tok;
+//             both dot products first bounded by the group's SwiGLU limit, if any)
 //   down:     Y[r][n] = h_r . Wd[n]                                (fp32)
 // Expert FFN shape: llm-atlas "Step-3.5-Flash", "Champs bruts du config.json"
 // (moe_intermediate_size, share_expert_dim, hidden_size); SiLU gating is the
@@ -152,6 +153,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   static_assert(kAL == 2, "two A fragments per wave and stage");
   const bool shared = group == g.E;
   const int shared_base = g.offsets[g.E];
+  const float lim = shared ? g.limit_shared : g.limit;
   const int npass = (MODE == 1 && shared) ? 2 : 1;
   size_t a_off[2];
   auto set_rows = [&](int pass) {
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         uint16_t* hp = reinterpret_cast<uint16_t*>(out) + row * hstride + blk * 32 + (lane & 15);
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const float hv = silu(acc[m][jb * 4 + f][i]) * acc[m][jb * 4 + 2 + f][i];
+          const float hv = swiglu(acc[m][jb * 4 + f][i], acc[m][jb * 4 + 2 + f][i], lim);
           const uint16_t hi = f32_to_bf16_bits(hv);
           hp[f * 16] = hi;
           if (shared)

@@ -41,6 +41,7 @@ struct GemmGeom {
   const int32_t* counts;      // [E+1] rows of each group
   int max_tiles;              // grid bound
   int tg;                     // token groups of 16 per tile (tile rows = 16 * tg)
+  float limit, limit_shared;  // SwiGLU limits of the routed / shared experts (0 = none)
 };
 
 // h[row][f] = silu(x W_gate^T) * (x W_up^T) for every permuted row; h is fp32

@@ -50,6 +50,7 @@ class MoELayer:
                  max_tokens: int, score: str = "softmax", renormalize: bool = True,
                  routed_scale: float = 1.0, bias_mode: str = "logit",
                  act_dtype: torch.dtype = torch.bfloat16, weight_dtype: str = "bf16",
+                 swiglu_limit: float = 0.0, swiglu_limit_shared: float = 0.0,
                  device: int = 0):
         self.lib = B.load()
         self.cfg = B.MoeLayerConfig(
@@ -58,7 +59,8 @@ class MoELayer:
             renormalize=int(bool(renormalize)), routed_scale=float(routed_scale),
             bias_mode=_BIAS[bias_mode],
             act_dtype=B.MOE_F32 if act_dtype == torch.float32 else B.MOE_BF16,
-            weight_dtype=B.MOE_INT4_G32 if weight_dtype == "int4_g32" else B.MOE_BF16)
+            weight_dtype=B.MOE_INT4_G32 if weight_dtype == "int4_g32" else B.MOE_BF16,
+            swiglu_limit=float(swiglu_limit), swiglu_limit_shared=float(swiglu_limit_shared))
         if act_dtype not in (torch.float32, torch.bfloat16):
             raise TypeError("act_dtype must be torch.float32 or torch.bfloat16")
         self.act_dtype = act_dtype
@@ -76,7 +78,9 @@ class MoELayer:
         return cls(shape.hidden, shape.experts, shape.top_k, shape.inter, shape.shared_inter,
                    max_tokens or shape.tokens, renormalize=shape.renormalize,
                    act_dtype=torch.float32 if shape.act_dtype == "f32" else torch.bfloat16,
-                   weight_dtype=shape.weight_dtype, device=device, **kw)
+                   weight_dtype=shape.weight_dtype, device=device,
+                   **{"swiglu_limit": getattr(shape, "swiglu_limit", 0.0),
+                      "swiglu_limit_shared": getattr(shape, "swiglu_limit_shared", 0.0), **kw})
 
     def close(self) -> None:
         if getattr(self, "_h", None):

@@ -101,8 +101,9 @@ def compare(inp, out, route, sample=None, score="softmax", renormalize=True, rou
             cache[e] = load(e)
         return cache[e]
 
+    lims = dict(swiglu_limit=shape.swiglu_limit, swiglu_limit_shared=shape.swiglu_limit_shared)
     y_ref, o_idx, o_w, l32 = oracle.forward(x64[rows], wr, bias, experts, shared, k, score,
-                                            renormalize, routed_scale, bias_mode)
+                                            renormalize, routed_scale, bias_mode, **lims)
     sel_scores = l32
     if bias is not None and bias_mode == "select":
         sel_scores = (l32.astype(np.float64) + bias[None, :]).astype(np.float32)
@@ -126,7 +127,8 @@ def compare(inp, out, route, sample=None, score="softmax", renormalize=True, rou
     flip = ~same
     if flip.any():
         y_f, *_ = oracle.forward(x64[rows][flip], wr, bias, experts, shared, k, score,
-                                 renormalize, routed_scale, bias_mode, force_idx=g_idx[rows][flip])
+                                 renormalize, routed_scale, bias_mode, force_idx=g_idx[rows][flip],
+                                 **lims)
         y_ref = y_ref.copy()
         y_ref[flip] = y_f
     y_gpu = out[torch.as_tensor(rows, device=out.device)].double().cpu().numpy()

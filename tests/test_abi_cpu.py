@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def _cfg(**kw):
@@ -48,6 +48,8 @@ def _cfg(**kw):
     (dict(shared_inter=-32), 2), (dict(max_tokens=0), 2), (dict(act_dtype=2), 3),
     (dict(weight_dtype=0), 3), (dict(score=5), 3), (dict(bias_mode=2), 3),
     (dict(routed_scale=0.0), 2), (dict(weight_dtype=2, inter=64), 2),
+    (dict(swiglu_limit=-1.0), 2), (dict(swiglu_limit_shared=float("inf")), 2),
+    (dict(swiglu_limit=float("nan")), 2),
 ])
 def test_config_validation(lib, kw, status):
     from sparse_mixture_experts_layer_amd import _binding as B

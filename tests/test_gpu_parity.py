@@ -263,3 +263,61 @@ def test_dense_ffn_as_one_expert(tokens):
     s = W["decode"].replace(name="dense_ffn", experts=1, top_k=1, inter=11264, shared_inter=0,
                             tokens=tokens)
     _run(s, sample=_spread(tokens, 8) if tokens > 64 else None)
+
+
+# ----------------------------------------------------------------- SwiGLU limits
+
+LIMITS = dict(swiglu_limit=0.5, swiglu_limit_shared=0.75)   # act on N(0, 1) projections
+
+
+@pytest.mark.parametrize("act,weights", [("f32", "bf16"), ("bf16", "bf16"), ("bf16", "int4_g32"),
+                                         ("f32", "int4_g32")])
+def test_tiny_swiglu_limits(act, weights):
+    """Limits small enough that most up and a third of the gate projections
+    are clamped, different for the routed and the shared expert, through each
+    streaming-kernel variant (fp32 h, bf16 h + remainder, INT4)."""
+    w = 128 if weights == "int4_g32" else 64
+    s = W["tiny"].replace(name=f"tiny_limits_{act}_{weights}", act_dtype=act, weight_dtype=weights,
+                          inter=w, shared_inter=w, **LIMITS)
+    _run(s)
+
+
+@pytest.mark.parametrize("tokens,inter,shared_inter", [(512, 64, 64), (4000, 96, 160)])
+def test_tiled_swiglu_limits(tokens, inter, shared_inter):
+    """The LDS-tiled GEMMs (128- and 256-row tiles) with both limits."""
+    s = TILED_SMALL.replace(name=f"tiled_limits_{tokens}", inter=inter, shared_inter=shared_inter,
+                            tokens=tokens, **LIMITS)
+    _run(s)
+
+
+def test_mtp_decode_32():
+    """A last layer's limits (7 routed, 16 shared) at the full shape, on
+    activations wide enough that both clamps act."""
+    _run(W["mtp_decode"])
+
+
+def test_mtp_decode_int4():
+    s = W["mtp_decode"].replace(name="mtp_int4", weight_dtype="int4_g32")
+    _run(s)
+
+
+def test_mtp_large_batch_sampled():
+    s = W["mtp_decode"].replace(name="mtp_4096", tokens=4096)   # ~114 rows per expert: tiled
+    _run(s, sample=_spread(4096, 10))
+
+
+def test_swiglu_limits_change_the_output():
+    """The limits of the last layers must matter on these inputs: the same
+    layer without them differs by far more than the tolerance."""
+    s = W["mtp_decode"]
+    inp = moe_synth.make_layer(s, seed=0, device="cuda")
+    outs = []
+    for lim in [(7.0, 16.0), (0.0, 0.0)]:
+        layer = make_layer(s, swiglu_limit=lim[0], swiglu_limit_shared=lim[1])
+        layer.pack_inputs(inp)
+        out, _ = run_gpu(layer, inp)
+        outs.append(out.float())
+    diff = (outs[0] - outs[1]).abs().max().item()
+    rms = outs[1].pow(2).mean().sqrt().item()
+    _say("limits on vs off", diff / rms)
+    assert diff > 0.2 * rms
