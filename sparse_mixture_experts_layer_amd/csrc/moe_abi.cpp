@@ -149,10 +149,15 @@ Plan make_plan(const moe_layer& L, int T) {
   // one workgroup dispatches small batches; larger ones use per-block counts
   p.large_dispatch = T > 1024;
   p.blk_hist = take(p.large_dispatch ? (size_t)moe::dispatch_blocks(T) * E * 4 : 0);
-  p.h = take((size_t)rows * p.hstride * 4);
+  // h: fp32 rows on the streaming bf16 path; bf16 in packed fragment order,
+  // with a 16-row gap per group and a tile of slack, on the tiled path
+  const size_t h_rows_tiled = moe::tiled_h_rows(rows, E);
+  p.h = take(p.tiled ? h_rows_tiled * p.hstride * 2 : (size_t)rows * p.hstride * 4);
   // bf16 remainder of the shared expert's h: bf16 weights and activations
   const bool lo_plane = p.has_shared && c.weight_dtype == MOE_BF16 && c.act_dtype == MOE_BF16;
-  p.h_lo = take(lo_plane ? (size_t)T * p.hstride * 2 : 0);
+  p.h_lo = take(!lo_plane ? 0
+                : p.tiled ? moe::tiled_h_rows(T, 0) * p.hstride * 2
+                          : (size_t)T * p.hstride * 2);
   p.y = take((size_t)rows * c.hidden * 4);
   p.total = o;
   return p;

@@ -57,8 +57,15 @@ hipError_t launch_down(const GemmGeom& g, bool int4, bool act_f32, const void* h
                        const uint16_t* h_lo, int hstride, float* y, hipStream_t s);
 
 // Large-batch variants: LDS-staged tiles of 128 or 256 rows (g.tg 8 or 16,
-// any other value is rejected), bf16 h; the shared group's h also gets a bf16
-// remainder plane h_lo ([T][hstride]).
+// any other value is rejected), bf16 h in packed fragment order: 1 KiB
+// fragments of 16 rows x 32 features, fragment (b, kb) at (b * hstride/32 +
+// kb) KiB, group e's row r in packed row 16 * (ceil(offsets[e]/16) + e) + r;
+// h needs tiled_h_rows(P + T, E) rows of hstride bf16.  The shared group's h
+// also gets a bf16 remainder plane h_lo, packed the same way by its row
+// (tiled_h_rows(T, 0) rows).
+inline size_t tiled_h_rows(int rows, int groups) {
+  return 16 * ((size_t)(rows + 15) / 16 + groups + 1) + 256;
+}
 hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32_t* row_tok,
                                uint16_t* h, uint16_t* h_lo, int hstride, hipStream_t s);
 hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_t* h_lo,
