@@ -91,6 +91,7 @@ __device__ __forceinline__ void barrier() {
 __device__ __forceinline__ void wait_vm_lgkm0(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0072); break;
     case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
     case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
     case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
@@ -109,7 +110,19 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   using TS = TileShape<TM>;
   constexpr int kAFrags = TS::kAFrags, kStageBytes = TS::kStageBytes;
   constexpr int kAL = TS::kAL, kBL = TS::kBL, kLoadsPerStage = TS::kLoads;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
+  // Gate/up with 256-row tiles fetches the gathered x rows as whole 128-byte
+  // lines: one wave-wide load takes 64 k of 8 rows (8 lanes per row) instead
+  // of 32 k of 16 rows, which halves the cache lines each load touches.  A
+  // line spans two k-steps, so A sits in two double-step slots (TM rows x 64
+  // k each) beside a 3-slot ring of B; the 16-byte chunks of a row are
+  // XOR-swizzled by row so that the MFMA operand reads stay free of bank
+  // conflicts.  Every other kernel keeps A and B together per k-step.
+  constexpr bool XL = MODE == 0 && TM == 256;
+  constexpr int kBSlot = kBFrags * kFragBytes;                    // 16 KiB
+  constexpr int kA2Bytes = TM * 128;                              // TM rows x 64 k
+  constexpr int kA2Loads = kA2Bytes / kFragBytes / TS::kWaves;    // 4 per wave
+  constexpr int kLdsBytes = XL ? kStages * kBSlot + 2 * kA2Bytes : kStages * kStageBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
   // Work order.  Workgroups are dealt round-robin over the 8 XCDs (each with
   // its own L2; all share the last-level cache).  Inside an expert the
@@ -163,11 +176,28 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   // this wave's two A fragments (rows 16*(2*wave) .. +31 of the tile); for the
   // shared group's down GEMM, pass 1 reads the lo plane
   static_assert(kAL == 2, "two A fragments per wave and stage");
+  static_assert(!XL || kA2Loads == 4, "four A line loads per wave and double step");
   const bool shared = group == g.E;
   const float lim = shared ? g.limit_shared : g.limit;
   const int npass = (MODE == 1 && shared) ? 2 : 1;
-  size_t a_off[2];
+  size_t a_off[XL ? 4 : 2];
   auto set_rows = [&](int pass) {
+    if (XL) {
+      // load u of this wave: tile rows 32*wave + 8u .. +7, lane -> row lane/8;
+      // the lane fetches 16-byte chunk q of the row's 128 bytes and writes it
+      // to LDS position lane, where the reader expects chunk
+      // (lane % 8) ^ s, s = (row % 8) ^ (row % 16 >= 8) (row within its fragment)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int r = 32 * wave + 8 * u + (lane >> 3);
+        if (r >= nrows) r = 0;  // any valid row: its C row is never stored
+        int tok = row_tok[row0 + r];
+        tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
+        const int q = (lane & 7) ^ (lane >> 3) ^ (u & 1);
+        a_off[u] = (size_t)tok * H + q * 8;
+      }
+      return;
+    }
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       if (MODE == 0) {
@@ -201,7 +231,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   // One LDS base per operand and stage; the fragments are told apart by the
   // instruction's immediate offset, which the global->LDS load adds to both
   // the global and the LDS address (two M0 writes per stage instead of six).
-  auto issue = [&](int kk, int stage) {
+  auto issue_kstep = [&](int kk, int stage) {
     uint8_t* st = lds + stage * kStageBytes;
     uint8_t* la = st + 2 * wave * kFragBytes;
     load_frag<0>(a_base + a_off[0] + (size_t)kk * kAStep, la);
@@ -216,14 +246,56 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
       load_frag<3 * kFragBytes>(gb, lb);
     }
   };
-  auto rd_a = [&](int stage, int m) {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + stage * kStageBytes +
-                                                     (wm * 4 + m) * kFragBytes + lane * 16));
+  // XL: B of k-step kk in ring slot kk % 3; A of k-steps 2d, 2d+1 in double
+  // slot d % 2 (its slot is free once both steps were read, at the barrier of
+  // step 2d+1, which is when double step d+2 is issued)
+  auto issue_b = [&](int kk, int slot) {
+    uint8_t* lb = lds + slot * kBSlot + kBL * wave * kFragBytes;
+    const uint8_t* gb = bsrc + (size_t)kk * 4 * kFragBytes;
+    load_frag<0>(gb, lb);
+    load_frag<kFragBytes>(gb, lb);
+    if (kBL == 4) {
+      load_frag<2 * kFragBytes>(gb, lb);
+      load_frag<3 * kFragBytes>(gb, lb);
+    }
   };
-  auto rd_b = [&](int stage, int j) {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(
-        lds + stage * kStageBytes + (kAFrags + wn * 8 + j) * kFragBytes + lane * 16));
+  auto issue_a2 = [&](int d, int dslot) {
+    uint8_t* la = lds + kStages * kBSlot + dslot * kA2Bytes + 4 * wave * kFragBytes;
+    const uint16_t* s0 = a_base + (size_t)d * 64;
+    load_frag<0>(s0 + a_off[0], la);
+    load_frag<kFragBytes>(reinterpret_cast<const uint8_t*>(s0 + a_off[1]) - kFragBytes, la);
+    load_frag<2 * kFragBytes>(reinterpret_cast<const uint8_t*>(s0 + a_off[2]) - 2 * kFragBytes, la);
+    load_frag<3 * kFragBytes>(reinterpret_cast<const uint8_t*>(s0 + a_off[3]) - 3 * kFragBytes, la);
   };
+  // all loads of k-step kk, in the order the wait counts assume
+  auto issue = [&](int kk) {
+    if (XL) {
+      issue_b(kk, kk % kStages);
+      if ((kk & 1) == 0) issue_a2(kk >> 1, (kk >> 1) & 1);
+    } else {
+      issue_kstep(kk, kk % kStages);
+    }
+  };
+  // XL: this lane's A operand (fragment row r = lane % 16, chunk c = lane / 16)
+  // in a double slot: 8-row block r / 8, row r % 8, swizzled chunk; the odd
+  // k-step's chunks are 4 further (bit 6 of the offset)
+  const int xr = lane & 15;
+  const int xa = (xr >> 3) * kFragBytes + (xr & 7) * 128 + 16 * ((lane >> 4) ^ (xr & 7) ^ (xr >> 3));
+  auto rd_a = [&](int kk, int m) {
+    const uint8_t* p =
+        XL ? lds + kStages * kBSlot + ((kk >> 1) & 1) * kA2Bytes + (wm * 4 + m) * 2 * kFragBytes +
+                 (xa ^ ((kk & 1) * 64))
+           : lds + (kk % kStages) * kStageBytes + (wm * 4 + m) * kFragBytes + lane * 16;
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+  };
+  auto rd_b = [&](int kk, int j) {
+    const uint8_t* p = XL ? lds + (kk % kStages) * kBSlot + (wn * 8 + j) * kFragBytes + lane * 16
+                          : lds + (kk % kStages) * kStageBytes + (kAFrags + wn * 8 + j) * kFragBytes +
+                                lane * 16;
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+  };
+  // loads issued for k-step s (per wave)
+  auto loads_of = [&](int s) { return XL ? kBL + ((s & 1) ? 0 : kA2Loads) : kLoadsPerStage; };
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -241,26 +313,24 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   auto step = [&](int kk, bf16x8(&ca)[4], bf16x8(&na)[4], bool do_issue, bool do_read, int vm) {
     wait_vm_lgkm0(vm);
     barrier();
-    if (do_issue) issue(kk + kStages, kk % kStages);
-    const int nst = (kk + 1) % kStages;
+    if (do_issue) issue(kk + kStages);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[m][j] = mfma16(ca[m], b[j], acc[m][j]);
       if (do_read) {
-        b[j] = rd_b(nst, j);
-        if (j < 4) na[j] = rd_a(nst, j);
+        b[j] = rd_b(kk + 1, j);
+        if (j < 4) na[j] = rd_a(kk + 1, j);
       }
     }
   };
-  // loads issued after stage kk+1 that may still be in flight at step kk
-  // (stages kk+2 .. kk+kStages-1 that exist)
-  auto vm_at = [&](int kk) {
-    int n = nk - kk - 2;
-    n = n < 0 ? 0 : (n > kStages - 2 ? kStages - 2 : n);
-    return n * kLoadsPerStage;
-  };
-  constexpr int kVmMain = (kStages - 2) * kLoadsPerStage;
+  // loads issued after k-step kk+1's that may still be in flight at step kk:
+  // those of k-step kk+2 (kStages == 3), if it exists
+  static_assert(kStages == 3, "one k-step of loads in flight past the one awaited");
+  auto vm_at = [&](int kk) { return kk + 2 < nk ? loads_of(kk + 2) : 0; };
+  // the same in the main loop, for an even kk and for kk + 1
+  constexpr int kVmEven = XL ? kBL + kA2Loads : kLoadsPerStage;
+  constexpr int kVmOdd = XL ? kBL : kLoadsPerStage;
 
   for (int pass = 0; pass < npass; ++pass) {
     // pass 1 (shared group, down GEMM) starts after the last step's barrier
@@ -268,8 +338,12 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     set_rows(pass);
     a_base = pass == 0 ? a_src : h_lo;
     const int pro = nk < kStages ? nk : kStages;
-    for (int s = 0; s < pro; ++s) issue(s, s);
-    wait_vm_lgkm0((pro - 1) * kLoadsPerStage);
+    int vm0 = 0;
+    for (int s = 0; s < pro; ++s) {
+      issue(s);
+      if (s > 0) vm0 += loads_of(s);
+    }
+    wait_vm_lgkm0(vm0);
     barrier();
 #pragma unroll
     for (int m = 0; m < 4; ++m) a0[m] = rd_a(0, m);
@@ -277,8 +351,8 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     for (int j = 0; j < 8; ++j) b[j] = rd_b(0, j);
     int kk = 0;
     for (; kk + kStages + 1 < nk; kk += 2) {
-      step(kk, a0, a1, true, true, kVmMain);
-      step(kk + 1, a1, a0, true, true, kVmMain);
+      step(kk, a0, a1, true, true, kVmEven);
+      step(kk + 1, a1, a0, true, true, kVmOdd);
     }
     for (; kk < nk; kk += 2) {
       step(kk, a0, a1, kk + kStages < nk, kk + 1 < nk, vm_at(kk));
