@@ -18,85 +18,113 @@
 namespace moe {
 namespace {
 
-// One workgroup = 4 waves; a wave computes 16*NT tokens x 16*NE experts over
-// one K slice.  Tokens are the MFMA A operand and router rows the B operand,
-// so a lane ends with one expert column of 4 token rows per tile.
-template <bool XF32, int NT, int NE>
+// Small batches: a workgroup computes 16*NT tokens x 16 experts over one K
+// slice, which its 4 waves split in 4 and add up through LDS.  Tokens are the
+// MFMA A operand and router rows the B operand, so a lane ends with one expert
+// column of 4 token rows per token group.  At these sizes the kernel is a
+// chain of memory latencies, so a wave issues the loads of up to kBatch
+// k-steps before their MFMAs, every load unconditional (rows past T or E read
+// row 0; their results are never stored).
+template <bool XF32, int NT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv,
                                                             const uint16_t* __restrict__ wr,
                                                             float* __restrict__ part, int T, int H,
                                                             int E, int kchunk) {
+  constexpr int kBatch = 4;
+  __shared__ f32x4 red[3][NT][kWave];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * 16 * NT;
-  const int e0 = (blockIdx.y * 4 + wave) * 16 * NE;
-  if (e0 >= E) return;
-  const int kbeg = blockIdx.z * kchunk;
+  const int e0 = blockIdx.y * 16;
+  // this wave's k-steps: [s0, s1) of the slice's kchunk / 32
+  const int nst = kchunk / 32, q = (nst + 3) / 4;
+  const int s0 = min(nst, wave * q), s1 = min(nst, s0 + q);
   const int kl = (lane >> 4) * 8;
+  const int kb = blockIdx.z * kchunk + kl;
 
   size_t xoff[NT];
-  bool xok[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int tok = t0 + t * 16 + (lane & 15);
-    xok[t] = tok < T;
-    xoff[t] = (size_t)(xok[t] ? tok : 0) * H + kl;
+    xoff[t] = (size_t)(tok < T ? tok : 0) * H + kb;
   }
-  const uint16_t* wrow[NE];
-  bool wok[NE];
+  const int e = e0 + (lane & 15);
+  const uint16_t* wrow = wr + (size_t)(e < E ? e : 0) * H + kb;
+  f32x4 acc[NT];
 #pragma unroll
-  for (int n = 0; n < NE; ++n) {
-    const int e = e0 + n * 16 + (lane & 15);
-    wok[n] = e < E;
-    wrow[n] = wr + (size_t)(wok[n] ? e : 0) * H + kl;
-  }
-  f32x4 acc[NT][NE];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int n = 0; n < NE; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k = kbeg; k < kbeg + kchunk; k += 32) {
-    u32x4 b[NE];
+  for (int sb = s0; sb < s1; sb += kBatch) {
+    u32x4 b[kBatch], a0[kBatch][NT], a1[kBatch][NT];
 #pragma unroll
-    for (int n = 0; n < NE; ++n) b[n] = wok[n] ? load16(wrow[n] + k) : u32x4{0, 0, 0, 0};
+    for (int d = 0; d < kBatch; ++d) {
+      const int k = 32 * min(sb + d, s1 - 1);  // past the end: reload the last step
+      b[d] = load16(wrow + k);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      u32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
-      if (XF32) {
-        if (xok[t]) {
+      for (int t = 0; t < NT; ++t) {
+        if (XF32) {
           const float* xp = reinterpret_cast<const float*>(xv) + xoff[t] + k;
-          const u32x4 a0 = load16(xp), a1 = load16(xp + 4);
+          a0[d][t] = load16(xp);
+          a1[d][t] = load16(xp + 4);
+        } else {
+          a0[d][t] = load16(reinterpret_cast<const uint16_t*>(xv) + xoff[t] + k);
+        }
+      }
+    }
+    // steps past the end contribute 0 x 0 (selected, not branched around:
+    // a branch would let the compiler sink their loads behind the MFMAs)
+#pragma unroll
+    for (int d = 1; d < kBatch; ++d) {
+      if (sb + d >= s1) {
+        b[d] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) a0[d][t] = a1[d][t] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kBatch; ++d) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        u32x4 ah, al;
+        if (XF32) {
           float v[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v[i] = __uint_as_float(a0[i]);
-            v[4 + i] = __uint_as_float(a1[i]);
+            v[i] = __uint_as_float(a0[d][t][i]);
+            v[4 + i] = __uint_as_float(a1[d][t][i]);
           }
           split_f32x8(v, ah, al);
+          acc[t] = mfma16(as_bf16x8(ah), as_bf16x8(b[d]), acc[t]);
+          acc[t] = mfma16(as_bf16x8(al), as_bf16x8(b[d]), acc[t]);
+        } else {
+          acc[t] = mfma16(as_bf16x8(a0[d][t]), as_bf16x8(b[d]), acc[t]);
         }
-      } else if (xok[t]) {
-        ah = load16(reinterpret_cast<const uint16_t*>(xv) + xoff[t] + k);
-      }
-#pragma unroll
-      for (int n = 0; n < NE; ++n) {
-        acc[t][n] = mfma16(as_bf16x8(ah), as_bf16x8(b[n]), acc[t][n]);
-        if (XF32) acc[t][n] = mfma16(as_bf16x8(al), as_bf16x8(b[n]), acc[t][n]);
       }
     }
   }
 
+  // waves 1-3 hand their sums to wave 0, which adds them in wave order
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[wave - 1][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 o = red[w][t][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] += o[i];
+    }
+  if (e >= E) return;
   float* dst = part + (size_t)blockIdx.z * T * E;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int n = 0; n < NE; ++n) {
-      const int e = e0 + n * 16 + (lane & 15);
-      if (e >= E) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + t * 16 + (lane >> 4) * 4 + i;
-        if (tok < T) dst[(size_t)tok * E + e] = acc[t][n][i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int tok = t0 + t * 16 + (lane >> 4) * 4 + i;
+      if (tok < T) dst[(size_t)tok * E + e] = acc[t][i];
     }
 }
 
@@ -220,18 +248,18 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   unsigned long long key[kMaxPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) v[i] = 0.f;
-  // K-slice partial sums, added in slice order; 4 slices of loads in flight
-  for (int s0 = 0; s0 < ks; s0 += 4) {
-    float ld[4][kMaxPerLane];
+  // K-slice partial sums, added in slice order; 8 slices of loads in flight
+  for (int s0 = 0; s0 < ks; s0 += 8) {
+    float ld[8][kMaxPerLane];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int i = 0; i < kMaxPerLane; ++i) {
         const int e = lane + i * kWave;
         ld[u][i] = (s0 + u < ks && e < E) ? part[((size_t)(s0 + u) * T + t) * E + e] : 0.f;
       }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int i = 0; i < kMaxPerLane; ++i) v[i] += ld[u][i];
   }
@@ -316,7 +344,7 @@ struct RouterShape {
 };
 RouterShape router_shape(bool x_f32, int T, int ksteps) {
   if (!x_f32 && T > 256 && ksteps % 2 == 0) return {4, 6, 3, true};
-  return {T <= 32 ? 2 : 4, T <= 256 ? 1 : 2, 4, false};
+  return {T <= 32 ? 2 : 4, 1, 1, false};
 }
 }  // namespace
 
@@ -337,17 +365,15 @@ hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* route
     return hipGetLastError();
   }
   dim3 block(256);
-#define MOE_ROUTER_CASE(XF, NT_, NE_)                                                         \
-  hipLaunchKernelGGL((router_logits_kernel<XF, NT_, NE_>), grid, block, 0, s, x, router_w, part, \
-                     T, H, E, kchunk)
+#define MOE_ROUTER_CASE(XF, NT_)                                                              \
+  hipLaunchKernelGGL((router_logits_kernel<XF, NT_>), grid, block, 0, s, x, router_w, part, T, H, \
+                     E, kchunk)
   if (x_f32) {
-    if (r.nt == 2) MOE_ROUTER_CASE(true, 2, 1);
-    else if (r.ne == 1) MOE_ROUTER_CASE(true, 4, 1);
-    else MOE_ROUTER_CASE(true, 4, 2);
+    if (r.nt == 2) MOE_ROUTER_CASE(true, 2);
+    else MOE_ROUTER_CASE(true, 4);
   } else {
-    if (r.nt == 2) MOE_ROUTER_CASE(false, 2, 1);
-    else if (r.ne == 1) MOE_ROUTER_CASE(false, 4, 1);
-    else MOE_ROUTER_CASE(false, 4, 2);
+    if (r.nt == 2) MOE_ROUTER_CASE(false, 2);
+    else MOE_ROUTER_CASE(false, 4);
   }
 #undef MOE_ROUTER_CASE
   return hipGetLastError();
