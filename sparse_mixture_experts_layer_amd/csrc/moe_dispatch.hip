@@ -7,14 +7,16 @@
 // article, architecture section); gathering each expert's tokens into
 // contiguous rows is how the expert FFNs become dense GEMMs.
 //
-// One workgroup of 16 waves; deterministic without global atomics:
+// One workgroup of 16 waves (up to 1024 tokens: a wave's slice is at most one
+// token per lane, whose choices the lane loads once, all in flight together);
+// deterministic without global atomics:
 //   1. wave w counts the pairs of its token slice per expert (LDS atomics:
 //      counts do not depend on their order);
 //   2. per expert, the wave counts are scanned in wave order, the expert
 //      totals are scanned in expert order;
-//   3. each wave walks its slice 64 tokens at a time; a pair's rank inside its
-//      expert is the number of lower lanes of the same step holding that
-//      expert (64-bit LDS masks + popcount) plus everything earlier.
+//   3. a pair's rank inside its expert is the number of lower lanes of the
+//      wave holding that expert (64-bit LDS masks + popcount) plus the counts
+//      of earlier waves.
 // The shared expert is group E: rows P .. P+T-1 hold tokens 0 .. T-1.
 #include "moe_common.hpp"
 #include "moe_kernels.hpp"
@@ -67,8 +69,20 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int P = T * k;
-  const int tw = (T + kDispWaves - 1) / kDispWaves;  // tokens per wave
+  const int tw = (T + kDispWaves - 1) / kDispWaves;  // tokens per wave, <= 64
   const int tbeg = min(T, wave * tw), tend = min(T, tbeg + tw);
+
+  // this lane's token and its choices: unconditional loads (a lane without a
+  // token re-reads token 0; choices past k re-read the last one), issued
+  // before the LDS is cleared so that their latency overlaps it
+  const int t = tbeg + lane;
+  const bool ok = lane < tw && t < tend;
+  const int tl = ok ? t : 0;
+  int ej[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) ej[j] = idx[(size_t)tl * k + (j < k ? j : k - 1)];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) ej[j] = ej[j] < 0 ? 0 : (ej[j] >= E ? E - 1 : ej[j]);
 
   for (int i = tid; i < kDispWaves * E; i += kDispThreads) {
     hist[i / E][i % E] = 0;
@@ -77,12 +91,12 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   __syncthreads();
 
   // 1. histogram per wave
-  for (int t = tbeg + lane; t < tend; t += kWave) {
-    for (int j = 0; j < k; ++j) {
-      int e = idx[(size_t)t * k + j];
-      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-      atomicAdd(&hist[wave][e], 1);
-    }
+  if (ok) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k)
+        __hip_atomic_fetch_add(&hist[wave][ej[j]], 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
 
@@ -123,48 +137,28 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   }
   if (tid == 0) ntiles_out[0] = total_tiles;
 
-  // 3. stable scatter, 64 tokens per wave step
-  const int steps = (tw + kWave - 1) / kWave;
-  for (int s = 0; s < steps; ++s) {
-    const int t = tbeg + s * kWave + lane;
-    const bool ok = t < tend;
-    int ej[kMaxTopK];
+  // 3. stable scatter: a pair's row = the wave's first row of its expert +
+  // the lanes below holding that expert (a token holds an expert once)
+  if (ok) {
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      ej[j] = 0;
-      if (j < k && ok) {
-        int e = idx[(size_t)t * k + j];
-        ej[j] = e < 0 ? 0 : (e >= E ? E - 1 : e);
-        atomicOr(&mask[wave][ej[j]], 1ull << lane);
-      }
-    }
-    __syncthreads();
-    int rank[kMaxTopK], cnt[kMaxTopK];
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k)
+        __hip_atomic_fetch_or(&mask[wave][ej[j]], 1ull << lane, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
+  if (ok) {
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-      rank[j] = -1;
-      cnt[j] = 0;
-      if (j < k && ok) {
-        const unsigned long long m = mask[wave][ej[j]];
-        rank[j] = __popcll(m & below);
-        cnt[j] = __popcll(m);
-        const int row = hist[wave][ej[j]] + rank[j];
+      if (j < k) {
+        const int row = hist[wave][ej[j]] + __popcll(mask[wave][ej[j]] & below);
         const int p = t * k + j;
         perm[row] = p;
         inv[p] = row;
         row_tok[row] = t;
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k && ok && rank[j] == 0) {
-        hist[wave][ej[j]] += cnt[j];
-        mask[wave][ej[j]] = 0ull;
-      }
-    }
-    __syncthreads();
   }
 
   if (has_shared)
@@ -333,6 +327,7 @@ hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int ha
 hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                            int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s) {
+  if (T < 1 || T > kDispThreads || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, idx, T, k, E, has_shared,
                      bm, counts, offsets, perm, inv, row_tok, tiles, ntiles);
   return hipGetLastError();
