@@ -176,10 +176,12 @@ moe_status_t moe_layer_forward(moe_layer_t layer, int32_t num_tokens, const void
 #define MOE_STAGE_EVENTS 6
 
 /* moe_layer_forward, and on `stream` also records stage_events[0] before the
- * router and stage_events[1..5] after the router (logits + top-k), dispatch,
- * gate/up GEMM, down GEMM and combine stages, so that
+ * router and stage_events[1..5] after the router, dispatch, gate/up GEMM,
+ * down GEMM and combine stages, so that
  * hipEventElapsedTime(stage_events[i], stage_events[i+1]) is the duration of
- * stage i.  stage_events holds MOE_STAGE_EVENTS events created by the caller
+ * stage i.  Top-k selection runs in one launch with the dispatch for batches
+ * of up to 1024 tokens (it is then timed in the dispatch stage) and with the
+ * router logits above that.  stage_events holds MOE_STAGE_EVENTS events created by the caller
  * (hipEventCreate); the same errors as moe_layer_forward, plus MOE_ERR_NULL
  * for a NULL array. */
 moe_status_t moe_layer_forward_timed(moe_layer_t layer, int32_t num_tokens, const void* x,

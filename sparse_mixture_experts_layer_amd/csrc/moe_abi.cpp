@@ -96,8 +96,8 @@ moe_status_t check_config(const moe_layer_config_t* c) {
 // Per-call plan and workspace layout.
 struct Plan {
   int T, P, ks, tg, max_tiles, has_shared, hstride, tiled;
-  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, blk_hist, h, h_lo, y,
-      total;
+  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, done, blk_hist, h,
+      h_lo, y, total;
   int large_dispatch;
 };
 
@@ -146,6 +146,7 @@ Plan make_plan(const moe_layer& L, int T) {
   p.row_tok = take((size_t)rows * 4);
   p.tiles = take((size_t)p.max_tiles * 4);
   p.ntiles = take(4);
+  p.done = take(4);
   // one workgroup dispatches small batches; larger ones use per-block counts
   p.large_dispatch = T > 1024;
   p.blk_hist = take(p.large_dispatch ? (size_t)moe::dispatch_blocks(T) * E * 4 : 0);
@@ -341,22 +342,30 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   const int E = c.num_experts, H = c.hidden, k = c.top_k;
 
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  // up to 1024 tokens, top-k and dispatch run as one launch (the router stage
+  // then ends after the logits); larger batches use the multi-workgroup
+  // dispatch after a separate top-k
+  int32_t* done = reinterpret_cast<int32_t*>(ws + p.done);
   hipError_t e = mark(0);
   if (e == hipSuccess)
     e = moe::launch_router_logits(f32, x, static_cast<const uint16_t*>(router_w), part, T, H, E,
-                                  p.ks, stream);
-  if (e == hipSuccess)
-    e = moe::launch_router_topk(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
-                                c.renormalize, c.routed_scale, idx, wts, gap, stream);
-  if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess) {
-    if (p.large_dispatch)
+                                  p.ks, p.large_dispatch ? nullptr : done, stream);
+  if (p.large_dispatch) {
+    if (e == hipSuccess)
+      e = moe::launch_router_topk(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
+                                  c.renormalize, c.routed_scale, idx, wts, gap, stream);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess)
       e = moe::launch_dispatch_large(idx, T, k, E, p.has_shared, 16 * p.tg,
                                      reinterpret_cast<int32_t*>(ws + p.blk_hist), counts, offsets,
                                      perm, inv, row_tok, tiles, ntiles, stream);
-    else
-      e = moe::launch_dispatch(idx, T, k, E, p.has_shared, 16 * p.tg, counts, offsets, perm, inv,
-                               row_tok, tiles, ntiles, stream);
+  } else {
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess)
+      e = moe::launch_topk_dispatch(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
+                                    c.renormalize, c.routed_scale, idx, wts, gap, done,
+                                    p.has_shared, 16 * p.tg, counts, offsets, perm, inv, row_tok,
+                                    tiles, ntiles, stream);
   }
   if (e == hipSuccess) e = mark(2);
   moe::GemmGeom g{};

@@ -20,6 +20,7 @@
 // The shared expert is group E: rows P .. P+T-1 hold tokens 0 .. T-1.
 #include "moe_common.hpp"
 #include "moe_kernels.hpp"
+#include "moe_topk.hpp"
 
 namespace moe {
 namespace {
@@ -55,13 +56,17 @@ __device__ int block_exclusive_scan(int* buf, int* total_slot, int n) {
   return *total_slot;
 }
 
-__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
+// The whole dispatch for up to 64 * NW tokens, run by one workgroup of NW
+// waves (the last one of the top-k + dispatch kernel).
+template <int NW>
+__device__ __forceinline__ void dispatch_body(
     const int32_t* __restrict__ idx, int T, int k, int E, int has_shared, int bm,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, int32_t* __restrict__ row_tok, int32_t* __restrict__ tiles,
     int32_t* __restrict__ ntiles_out) {
-  __shared__ int hist[kDispWaves][kMaxExperts];                 // 32 KiB
-  __shared__ unsigned long long mask[kDispWaves][kMaxExperts];  // 64 KiB
+  constexpr int NTH = NW * kWave;
+  __shared__ int hist[NW][kMaxExperts];                 // 2 KiB per wave
+  __shared__ unsigned long long mask[NW][kMaxExperts];  // 4 KiB per wave
   __shared__ int tot[kMaxExperts + 1];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int ntile[kMaxExperts + 1];
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int P = T * k;
-  const int tw = (T + kDispWaves - 1) / kDispWaves;  // tokens per wave, <= 64
+  const int tw = (T + NW - 1) / NW;  // tokens per wave, <= 64
   const int tbeg = min(T, wave * tw), tend = min(T, tbeg + tw);
 
   // this lane's token and its choices: unconditional loads (a lane without a
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) ej[j] = ej[j] < 0 ? 0 : (ej[j] >= E ? E - 1 : ej[j]);
 
-  for (int i = tid; i < kDispWaves * E; i += kDispThreads) {
+  for (int i = tid; i < NW * E; i += NTH) {
     hist[i / E][i % E] = 0;
     mask[i / E][i % E] = 0ull;
   }
@@ -101,23 +106,23 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   __syncthreads();
 
   // 2. per-expert scan over waves, then scan over experts
-  if (tid < E) {
+  for (int ex = tid; ex < E; ex += NTH) {
     int run = 0;
-    for (int w = 0; w < kDispWaves; ++w) {
-      const int c = hist[w][tid];
-      hist[w][tid] = run;
+    for (int w = 0; w < NW; ++w) {
+      const int c = hist[w][ex];
+      hist[w][ex] = run;
       run += c;
     }
-    tot[tid] = run;
-    off[tid] = run;
+    tot[ex] = run;
+    off[ex] = run;
   }
   __syncthreads();
   block_exclusive_scan(off, &scan_total, E);
-  if (tid < E) {
-    counts[tid] = tot[tid];
-    offsets[tid] = off[tid];
-    ntile[tid] = (tot[tid] + bm - 1) / bm;
-    for (int w = 0; w < kDispWaves; ++w) hist[w][tid] += off[tid];
+  for (int ex = tid; ex < E; ex += NTH) {
+    counts[ex] = tot[ex];
+    offsets[ex] = off[ex];
+    ntile[ex] = (tot[ex] + bm - 1) / bm;
+    for (int w = 0; w < NW; ++w) hist[w][ex] += off[ex];
   }
   if (tid == 0) {
     counts[E] = has_shared ? T : 0;
@@ -130,10 +135,10 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   // tile list: groups in order 0..E, m-tiles in order inside a group
   const int total_tiles = block_exclusive_scan(ntile, &scan_total, E + 1);
   // ntile[] now holds each group's first tile; the tile count is recomputed.
-  if (tid <= E) {
-    const int c = tid < E ? tot[tid] : (has_shared ? T : 0);
+  for (int gr = tid; gr <= E; gr += NTH) {
+    const int c = gr < E ? tot[gr] : (has_shared ? T : 0);
     const int nt = (c + bm - 1) / bm;
-    for (int m = 0; m < nt; ++m) tiles[ntile[tid] + m] = (tid << 16) | m;
+    for (int m = 0; m < nt; ++m) tiles[ntile[gr] + m] = (gr << 16) | m;
   }
   if (tid == 0) ntiles_out[0] = total_tiles;
 
@@ -162,7 +167,39 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   }
 
   if (has_shared)
-    for (int t = tid; t < T; t += kDispThreads) row_tok[P + t] = t;
+    for (int t = tid; t < T; t += NTH) row_tok[P + t] = t;
+}
+
+// Top-k for NW tokens per workgroup (one wave each), then the workgroup that
+// finishes last runs the dispatch: one launch less on the path of small
+// batches.  `done` counts finished workgroups; the router logits kernel
+// clears it earlier on the same stream.  After the workgroup barrier (its
+// waves' choices are in this XCD's L2), one thread releases them device-wide
+// and counts the workgroup; the thread that counts last acquires every
+// workgroup's choices for its own.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
+    const float* __restrict__ part, int ks, const float* __restrict__ bias, int bias_mode, int T,
+    int E, int k, int score, int renorm, float scale, int32_t* __restrict__ idx,
+    float* __restrict__ wout, float* __restrict__ gap, int32_t* __restrict__ done,
+    int has_shared, int bm, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_tok,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles_out) {
+  __shared__ int last;
+  const int t = blockIdx.x * NW + (threadIdx.x >> 6);
+  if (t < T) topk_token(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this XCD's L2 -> memory
+    const bool l = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (int)gridDim.x - 1;
+    if (l) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    last = l;
+  }
+  __syncthreads();
+  if (!last) return;
+  dispatch_body<NW>(idx, T, k, E, has_shared, bm, counts, offsets, perm, inv, row_tok, tiles,
+                    ntiles_out);
 }
 
 // ---------------------------------------------------------------- large batches
@@ -324,13 +361,23 @@ hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int ha
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
-                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s) {
+hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, int bias_mode, int T,
+                                int E, int k, int score, int renorm, float scale, int32_t* idx,
+                                float* w, float* gap, int32_t* done, int has_shared, int bm,
+                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s) {
   if (T < 1 || T > kDispThreads || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, idx, T, k, E, has_shared,
-                     bm, counts, offsets, perm, inv, row_tok, tiles, ntiles);
+  // 4 tokens per workgroup up to 256 tokens (the top-k waves spread over more
+  // CUs), 16 above
+#define MOE_TD(NW)                                                                              \
+  hipLaunchKernelGGL(topk_dispatch_kernel<NW>, dim3((T + NW - 1) / NW), dim3(NW * 64), 0, s,  \
+                     part, ks, bias, bias_mode, T, E, k, score, renorm, scale, idx, w, gap, done, \
+                     has_shared, bm, counts, offsets, perm, inv, row_tok, tiles, ntiles)
+  if (T <= 4 * kWave) MOE_TD(4);
+  else MOE_TD(kDispWaves);
+#undef MOE_TD
   return hipGetLastError();
 }
+
 
 }  // namespace moe

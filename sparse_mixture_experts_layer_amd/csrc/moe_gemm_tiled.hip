@@ -180,7 +180,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   const bool shared = group == g.E;
   const float lim = shared ? g.limit_shared : g.limit;
   const int npass = (MODE == 1 && shared) ? 2 : 1;
-  size_t a_off[XL ? 4 : 2];
+  size_t a_off[4];  // XL: one row per line load; otherwise the first two
   auto set_rows = [&](int pass) {
     if (XL) {
       // load u of this wave: tile rows 32*wave + 8u .. +7, lane -> row lane/8;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   };
   // all loads of k-step kk, in the order the wait counts assume
   auto issue = [&](int kk) {
-    if (XL) {
+    if constexpr (XL) {
       issue_b(kk, kk % kStages);
       if ((kk & 1) == 0) issue_a2(kk >> 1, (kk >> 1) & 1);
     } else {

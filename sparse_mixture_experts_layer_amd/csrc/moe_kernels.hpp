@@ -10,17 +10,24 @@ namespace moe {
 // ---- router: logits (fp32 partial sums over KS slices of H) + top-k ----------
 // Workgroups of the router logits kernel for a batch (before the K split).
 int router_blocks(bool x_f32, int T, int E);
+// done, if not null, is set to 0 (the counter of launch_topk_dispatch).
 hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
-                                int T, int H, int E, int ks, hipStream_t s);
+                                int T, int H, int E, int ks, int32_t* done, hipStream_t s);
 hipError_t launch_router_topk(const float* part, int ks, const float* bias, int bias_mode, int T,
                               int E, int k, int score, int renorm, float scale, int32_t* idx,
                               float* w, float* gap, hipStream_t s);
 
 // ---- dispatch: counts, offsets, stable permutation, GEMM tile list ----------
 // counts/offsets have E+1 / E+2 entries (group E = shared expert, T rows).
-hipError_t launch_dispatch(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
-                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s);
+// Top-k (as launch_router_topk) and the dispatch in one launch, T <= 1024:
+// the last workgroup to finish its tokens' top-k runs the dispatch as one
+// workgroup.  done is a device counter that must read 0 at launch
+// (launch_router_logits clears it).
+hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, int bias_mode, int T,
+                                int E, int k, int score, int renorm, float scale, int32_t* idx,
+                                float* w, float* gap, int32_t* done, int has_shared, int bm,
+                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s);
 
 // Multi-workgroup variant for large batches (same outputs); blk_hist is
 // scratch of dispatch_blocks(T) * E int32.

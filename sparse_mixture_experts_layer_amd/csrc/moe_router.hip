@@ -12,6 +12,7 @@
 // (need_fp32_gate).  fp32 activations are split into bf16 hi + lo first.
 #include "moe_common.hpp"
 #include "moe_kernels.hpp"
+#include "moe_topk.hpp"
 
 #include <math.h>
 
@@ -29,9 +30,11 @@ template <bool XF32, int NT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv,
                                                             const uint16_t* __restrict__ wr,
                                                             float* __restrict__ part, int T, int H,
-                                                            int E, int kchunk) {
+                                                            int E, int kchunk,
+                                                            int32_t* __restrict__ done) {
   constexpr int kBatch = 4;
   __shared__ f32x4 red[3][NT][kWave];
+  if (done && blockIdx.x + blockIdx.y + blockIdx.z + threadIdx.x == 0) *done = 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * 16 * NT;
   const int e0 = blockIdx.y * 16;
@@ -137,7 +140,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 template <int NT, int NE, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void router_logits_wide_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ part,
-    int T, int H, int E, int kchunk) {
+    int T, int H, int E, int kchunk, int32_t* __restrict__ done) {
+  if (done && blockIdx.x + blockIdx.y + blockIdx.z + threadIdx.x == 0) *done = 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * 16 * NT;
   const int e0 = (blockIdx.y * NW + wave) * 16 * NE;
@@ -196,141 +200,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 }
 
-// Orderable key of (score, expert): larger key = larger score, and on equal
-// scores the lower expert index.  NaN ranks as -inf.
-__device__ __forceinline__ unsigned long long rank_key(float s, int e) {
-  if (s != s) s = -INFINITY;
-  uint32_t u = __float_as_uint(s);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_score(unsigned long long key) {
-  uint32_t u = (uint32_t)(key >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-  return __uint_as_float(u);
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const unsigned long long o = __shfl_xor(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
-
-constexpr int kMaxPerLane = kMaxExperts / kWave;  // 8
-
-// One wave per token.  Expert e lives in lane e % 64, slot e / 64.  Each round
-// takes the wave-wide largest remaining key; the owner lane retires it.
+// One wave per token.
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ part, int ks, const float* __restrict__ bias, int bias_mode, int T,
     int E, int k, int score, int renorm, float scale, int32_t* __restrict__ idx,
     float* __restrict__ wout, float* __restrict__ gap) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-
-  float lg[kMaxPerLane], v[kMaxPerLane];
-  unsigned long long key[kMaxPerLane];
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) v[i] = 0.f;
-  // K-slice partial sums, added in slice order; 8 slices of loads in flight
-  for (int s0 = 0; s0 < ks; s0 += 8) {
-    float ld[8][kMaxPerLane];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + i * kWave;
-        ld[u][i] = (s0 + u < ks && e < E) ? part[((size_t)(s0 + u) * T + t) * E + e] : 0.f;
-      }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) v[i] += ld[u][i];
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + i * kWave;
-    lg[i] = -INFINITY;
-    key[i] = 0ull;  // below every real key
-    if (e < E) {
-      const float b = bias ? bias[e] : 0.f;
-      const float l = (bias && bias_mode == 0) ? v[i] + b : v[i];
-      lg[i] = l;
-      key[i] = rank_key((bias && bias_mode == 1) ? l + b : l, e);
-    }
-  }
-
-  // softmax reference point: the largest logit (selection may use biased scores)
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) m = fmaxf(m, lg[i]);
-  m = wave_max(m);
-
-  float denom = 0.f, kth = 0.f;
-  int my_e = 0;
-  float my_p = 0.f;
-  for (int r = 0; r < k; ++r) {
-    unsigned long long best = 0ull;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(0xffffffffu - (uint32_t)best);
-    const int owner = e & 63, slot = e >> 6;
-    float l = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (i == slot) l = lg[i];
-    l = __shfl(l, owner);
-    if (lane == owner) {
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
-        if (i == slot) key[i] = 0ull;
-    }
-    const float p = score == 0 ? expf(l - m) : 1.f / (1.f + expf(-l));
-    denom += p;
-    if (lane == r) {
-      my_e = e;
-      my_p = p;
-    }
-    if (r == k - 1) kth = key_score(best);
-  }
-  unsigned long long nxt = 0ull;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) nxt = key[i] > nxt ? key[i] : nxt;
-  nxt = wave_max_u64(nxt);
-
-  if (!renorm) {
-    if (score == 0) {
-      float z = 0.f;
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
-        if (lane + i * kWave < E) z += expf(lg[i] - m);
-      denom = wave_sum(z);
-    } else {
-      denom = 1.f;
-    }
-  }
-  if (lane < k) {
-    idx[(size_t)t * k + lane] = my_e;
-    wout[(size_t)t * k + lane] = my_p * (scale / denom);
-  }
-  if (lane == 0) gap[t] = nxt ? kth - key_score(nxt) : INFINITY;
+  topk_token(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
 }
 
 }  // namespace
@@ -354,20 +231,20 @@ int router_blocks(bool x_f32, int T, int E) {
 }
 
 hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
-                                int T, int H, int E, int ks, hipStream_t s) {
+                                int T, int H, int E, int ks, int32_t* done, hipStream_t s) {
   const int kchunk = H / ks;
   // the wide kernel takes an even number of 32-wide k-steps per slice
   const RouterShape r = router_shape(x_f32, T, kchunk / 32);
   dim3 grid((T + 16 * r.nt - 1) / (16 * r.nt), (E + 16 * r.ne * r.nw - 1) / (16 * r.ne * r.nw), ks);
   if (r.wide) {
     hipLaunchKernelGGL((router_logits_wide_kernel<4, 6, 3>), grid, dim3(64 * 3), 0, s,
-                       static_cast<const uint16_t*>(x), router_w, part, T, H, E, kchunk);
+                       static_cast<const uint16_t*>(x), router_w, part, T, H, E, kchunk, done);
     return hipGetLastError();
   }
   dim3 block(256);
 #define MOE_ROUTER_CASE(XF, NT_)                                                              \
   hipLaunchKernelGGL((router_logits_kernel<XF, NT_>), grid, block, 0, s, x, router_w, part, T, H, \
-                     E, kchunk)
+                     E, kchunk, done)
   if (x_f32) {
     if (r.nt == 2) MOE_ROUTER_CASE(true, 2);
     else MOE_ROUTER_CASE(true, 4);

@@ -1,0 +1,166 @@
+// Per-token top-k selection over the router logits, shared by the top-k
+// kernel and the fused top-k + dispatch kernel.
+//
+// Source: llm-atlas "Step-3.5-Flash", table "Champs bruts du config.json"
+// (moe_top_k, norm_expert_weight, moe_router_activation,
+// moe_router_scaling_factor, use_moe_router_bias).  Readings where the pages
+// are silent: ties go to the lower expert index; the bias is added to the
+// logits (bias_mode 0) or to the selection scores only (bias_mode 1).
+#pragma once
+
+#include "moe_common.hpp"
+
+#include <math.h>
+
+namespace moe {
+
+// Orderable key of (score, expert): larger key = larger score, and on equal
+// scores the lower expert index.  NaN ranks as -inf.
+__device__ __forceinline__ unsigned long long rank_key(float s, int e) {
+  if (s != s) s = -INFINITY;
+  uint32_t u = __float_as_uint(s);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_score(unsigned long long key) {
+  uint32_t u = (uint32_t)(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const unsigned long long o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+constexpr int kMaxPerLane = kMaxExperts / kWave;  // 8
+
+// One wave selects for token t.  Expert e lives in lane e % 64, slot e / 64.
+// The logits are the sum of the ks K-slice partials part[s][t][e], added in
+// slice order.  Each round takes the wave-wide largest remaining key; the
+// owner lane retires it.  Writes idx[t][j], wout[t][j] (j in descending
+// order) and gap[t].
+__device__ __forceinline__ void topk_token(const float* __restrict__ part, int ks,
+                                           const float* __restrict__ bias, int bias_mode, int T,
+                                           int E, int k, int score, int renorm, float scale, int t,
+                                           int32_t* __restrict__ idx, float* __restrict__ wout,
+                                           float* __restrict__ gap) {
+  const int lane = threadIdx.x & 63;
+  float lg[kMaxPerLane], v[kMaxPerLane];
+  unsigned long long key[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) v[i] = 0.f;
+  // K-slice partial sums, added in slice order; 8 slices of loads in flight
+  for (int s0 = 0; s0 < ks; s0 += 8) {
+    float ld[8][kMaxPerLane];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + i * kWave;
+        ld[u][i] = (s0 + u < ks && e < E) ? part[((size_t)(s0 + u) * T + t) * E + e] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i) v[i] += ld[u][i];
+  }
+  // bias of each slot: all loads first (clamped index), then their uses
+  float bv[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) bv[i] = 0.f;
+  if (bias) {
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + i * kWave;
+      bv[i] = bias[e < E ? e : E - 1];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + i * kWave;
+    lg[i] = -INFINITY;
+    key[i] = 0ull;  // below every real key
+    if (e < E) {
+      const float b = bv[i];
+      const float l = (bias && bias_mode == 0) ? v[i] + b : v[i];
+      lg[i] = l;
+      key[i] = rank_key((bias && bias_mode == 1) ? l + b : l, e);
+    }
+  }
+
+  // softmax reference point: the largest logit (selection may use biased scores)
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) m = fmaxf(m, lg[i]);
+  m = wave_max(m);
+
+  float denom = 0.f, kth = 0.f;
+  int my_e = 0;
+  float my_p = 0.f;
+  for (int r = 0; r < k; ++r) {
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xffffffffu - (uint32_t)best);
+    const int owner = e & 63, slot = e >> 6;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i)
+      if (i == slot) l = lg[i];
+    l = __shfl(l, owner);
+    if (lane == owner) {
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (i == slot) key[i] = 0ull;
+    }
+    const float p = score == 0 ? expf(l - m) : 1.f / (1.f + expf(-l));
+    denom += p;
+    if (lane == r) {
+      my_e = e;
+      my_p = p;
+    }
+    if (r == k - 1) kth = key_score(best);
+  }
+  unsigned long long nxt = 0ull;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) nxt = key[i] > nxt ? key[i] : nxt;
+  nxt = wave_max_u64(nxt);
+
+  if (!renorm) {
+    if (score == 0) {
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (lane + i * kWave < E) z += expf(lg[i] - m);
+      denom = wave_sum(z);
+    } else {
+      denom = 1.f;
+    }
+  }
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_e;
+    wout[(size_t)t * k + lane] = my_p * (scale / denom);
+  }
+  if (lane == 0) gap[t] = nxt ? kth - key_score(nxt) : INFINITY;
+}
+
+}  // namespace moe
