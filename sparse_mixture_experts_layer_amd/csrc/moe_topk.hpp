@@ -29,25 +29,69 @@ __device__ __forceinline__ float key_score(unsigned long long key) {
   return __uint_as_float(u);
 }
 
+// Wave-wide reductions without LDS traffic: lane i ^ 1 and i ^ 2 through
+// DPP quad permutations, i ^ 4 / i ^ 8 through the 8- and 16-lane mirrors
+// (equivalent once every quad / octet holds one value), then the rows of 16
+// and the halves of 32 through gfx950's permlane swaps.  Every lane ends with
+// the same bits (each step combines two equal-structured partials with a
+// commutative operation).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
+}
+
+template <class F>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, F op) {
+  v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp<0x141>(v));  // row_half_mirror
+  v = op(v, dpp<0x140>(v));  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r[0], r[1]);
+  auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(h[0], h[1]);
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const unsigned long long o = __shfl_xor(v, m);
-    v = o > v ? o : v;
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  auto take = [&](uint32_t lo2, uint32_t hi2) {
+    const unsigned long long o = ((unsigned long long)hi2 << 32) | lo2;
+    const unsigned long long c = ((unsigned long long)hi << 32) | lo;
+    const unsigned long long m = o > c ? o : c;
+    lo = (uint32_t)m;
+    hi = (uint32_t)(m >> 32);
+  };
+  take(dpp<0xB1>(lo), dpp<0xB1>(hi));
+  take(dpp<0x4E>(lo), dpp<0x4E>(hi));
+  take(dpp<0x141>(lo), dpp<0x141>(hi));
+  take(dpp<0x140>(lo), dpp<0x140>(hi));
+  {
+    auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    lo = rl[0];
+    hi = rh[0];
+    take(rl[1], rh[1]);
   }
-  return v;
+  {
+    auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    lo = rl[0];
+    hi = rh[0];
+    take(rl[1], rh[1]);
+  }
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 
 constexpr int kMaxPerLane = kMaxExperts / kWave;  // 8
@@ -120,13 +164,16 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
     best = wave_max_u64(best);
+    // every lane holds the same best: make it scalar
+    best = ((unsigned long long)__builtin_amdgcn_readfirstlane((uint32_t)(best >> 32)) << 32) |
+           __builtin_amdgcn_readfirstlane((uint32_t)best);
     const int e = (int)(0xffffffffu - (uint32_t)best);
     const int owner = e & 63, slot = e >> 6;
     float l = 0.f;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i)
       if (i == slot) l = lg[i];
-    l = __shfl(l, owner);
+    l = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(l), owner));
     if (lane == owner) {
 #pragma unroll
       for (int i = 0; i < kMaxPerLane; ++i)
