@@ -115,8 +115,9 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   // of 32 k of 16 rows, which halves the cache lines each load touches.  A
   // line spans two k-steps, so A sits in two double-step slots (TM rows x 64
   // k each) beside a 3-slot ring of B; the 16-byte chunks of a row are
-  // XOR-swizzled by row so that the MFMA operand reads stay free of bank
-  // conflicts.  Every other kernel keeps A and B together per k-step.
+  // XOR-swizzled by the row's index within its 8-row block so that the MFMA
+  // operand reads stay free of bank conflicts.  Every other kernel keeps A
+  // and B together per k-step.
   constexpr bool XL = MODE == 0 && TM == 256;
   constexpr int kBSlot = kBFrags * kFragBytes;                    // 16 KiB
   constexpr int kA2Bytes = TM * 128;                              // TM rows x 64 k
@@ -185,15 +186,14 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     if (XL) {
       // load u of this wave: tile rows 32*wave + 8u .. +7, lane -> row lane/8;
       // the lane fetches 16-byte chunk q of the row's 128 bytes and writes it
-      // to LDS position lane, where the reader expects chunk
-      // (lane % 8) ^ s, s = (row % 8) ^ (row % 16 >= 8) (row within its fragment)
+      // to LDS position lane, where the reader expects chunk (lane % 8) ^ (row % 8)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         int r = 32 * wave + 8 * u + (lane >> 3);
         if (r >= nrows) r = 0;  // any valid row: its C row is never stored
         int tok = row_tok[row0 + r];
         tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
-        const int q = (lane & 7) ^ (lane >> 3) ^ (u & 1);
+        const int q = (lane & 7) ^ (lane >> 3);
         a_off[u] = (size_t)tok * H + q * 8;
       }
       return;
@@ -277,10 +277,12 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     }
   };
   // XL: this lane's A operand (fragment row r = lane % 16, chunk c = lane / 16)
-  // in a double slot: 8-row block r / 8, row r % 8, swizzled chunk; the odd
-  // k-step's chunks are 4 further (bit 6 of the offset)
+  // in a double slot: 8-row block r / 8, row r % 8, chunk c ^ (r % 8) (a
+  // swizzle measured free of bank conflicts for these 16-byte reads; one that
+  // also mixed in r / 8 was not); the odd k-step's chunks are 4 further
+  // (bit 6 of the offset)
   const int xr = lane & 15;
-  const int xa = (xr >> 3) * kFragBytes + (xr & 7) * 128 + 16 * ((lane >> 4) ^ (xr & 7) ^ (xr >> 3));
+  const int xa = (xr >> 3) * kFragBytes + (xr & 7) * 128 + 16 * ((lane >> 4) ^ (xr & 7));
   auto rd_a = [&](int kk, int m) {
     const uint8_t* p =
         XL ? lds + kStages * kBSlot + ((kk >> 1) & 1) * kA2Bytes + (wm * 4 + m) * 2 * kFragBytes +
