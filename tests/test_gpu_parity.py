@@ -192,6 +192,16 @@ def test_large_batch_dispatch(tokens, act):
     _run(s)
 
 
+@pytest.mark.parametrize("tokens", [64, 700])
+def test_max_experts_and_top_k(tokens):
+    """The largest expert count and top-k the boundary accepts (512, 16): every
+    top-k slot of every lane in use, 512-entry dispatch histograms, with 4-
+    and 16-token top-k + dispatch workgroups."""
+    s = W["tiny"].replace(name=f"max_e_k_{tokens}", act_dtype="bf16", experts=512, top_k=16,
+                          tokens=tokens)
+    _run(s)
+
+
 # ----------------------------------------------------------------- full Step-3.5-Flash shapes
 
 def _spread(T, n, seed=0):
@@ -223,11 +233,13 @@ def test_decode_ragged(tokens):
     _run(W["decode"], tokens=tokens, max_tokens=32)
 
 
-@pytest.mark.parametrize("tokens", [128, 257, 1025])
+@pytest.mark.parametrize("tokens", [128, 257, 1024, 1025])
 def test_mid_size_batches_sampled(tokens):
     """Batch sizes between decode and prefill at the full layer shape: 128
-    (2 token groups per tile), 257 (first size on the wide router kernel),
-    1025 (first size on the multi-workgroup dispatch, 4 token groups)."""
+    (2 token groups per tile), 257 (first size on the wide router kernel and
+    on 16-token top-k + dispatch workgroups), 1024 (last size of the fused
+    top-k + dispatch: 64 tokens per dispatching wave), 1025 (first size on
+    the multi-workgroup dispatch, 4 token groups)."""
     s = W["decode"].replace(name=f"mid_{tokens}", tokens=tokens)
     _run(s, sample=_spread(tokens, 10))
 
