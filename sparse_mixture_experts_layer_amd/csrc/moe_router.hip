@@ -12,6 +12,7 @@
 // (need_fp32_gate).  fp32 activations are split into bf16 hi + lo first.
 #include "moe_common.hpp"
 #include "moe_kernels.hpp"
+#include "moe_lds.hpp"
 #include "moe_topk.hpp"
 
 #include <math.h>
@@ -131,73 +132,128 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
     }
 }
 
-// Large batches, bf16 x: a workgroup of NW waves covers 16*NT tokens and
-// NW*16*NE experts (all 288 with NT=4, NE=6, NW=3), so per k-step a wave loads
-// NT + NE fragments for NT*NE MFMAs (the NT x fragments are shared by the
-// workgroup's waves through L1).  The loads of step k+32 are issued before
-// the MFMAs of step k.  Rows past T or E read row 0; their results are never
-// stored.  kchunk / 32 must be even.
-template <int NT, int NE, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void router_logits_wide_kernel(
+// Large batches, bf16 x: LDS-staged tiles of 256 tokens x 288 experts (all
+// of Step-3.5-Flash's router) over one K slice, so each router row is fetched
+// once per 256 tokens instead of once per 64.  8 waves, wave (wt, we) = (wave
+// % 4, wave / 4) owns tokens 64*wt .. +63 and experts 144*we .. +143 (4 x 9
+// fragments of 16x16, 144 fp32 accumulators per lane).  K advances 32 per
+// step through a 3-slot LDS ring: 16 x fragments and 18 router fragments of
+// 1 KiB, written by wave-wide global->LDS loads (every wave loads 2 x and 3
+// router fragments; waves 6-7 fill 6 spare slots with row 0, so that every
+// wave has the same wait counts); two steps stay in flight and the next
+// step's fragments are read into registers during the current MFMAs.  Rows
+// past T or E read a valid row; their results are never stored.
+constexpr int kRlTokens = 256, kRlExperts = 288;
+constexpr int kRlAFrags = kRlTokens / 16, kRlBFrags = kRlExperts / 16;  // 16, 18
+constexpr int kRlBSlots = 24;                                            // 3 per wave
+constexpr int kRlStage = (kRlAFrags + kRlBSlots) * kFragBytes;          // 40 KiB
+constexpr int kRlStages = 3;
+
+__global__ __launch_bounds__(512, 1) void router_logits_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ part,
     int T, int H, int E, int kchunk, int32_t* __restrict__ done) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRlStages * kRlStage];
   if (done && blockIdx.x + blockIdx.y + blockIdx.z + threadIdx.x == 0) *done = 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * 16 * NT;
-  const int e0 = (blockIdx.y * NW + wave) * 16 * NE;
-  if (e0 >= E) return;
-  const int kbeg = blockIdx.z * kchunk, kend = kbeg + kchunk;
+  const int wt = wave & 3, we = wave >> 2;
+  const int t0 = blockIdx.x * kRlTokens, e0 = blockIdx.y * kRlExperts;
+  const int kbeg = blockIdx.z * kchunk, nk = kchunk / 32;
   const int kl = (lane >> 4) * 8;
-  const uint16_t* xrow[NT];
-  const uint16_t* wrow[NE];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tok = t0 + t * 16 + (lane & 15);
-    xrow[t] = x + (size_t)(tok < T ? tok : 0) * H + kl;
+  // this wave's loads per step: x fragments 2*wave, 2*wave+1; router
+  // fragments (or spare slots) 3*wave .. 3*wave+2
+  constexpr int per_step = 5;
+  const uint16_t* a0p;
+  const uint16_t* a1p;
+  {
+    int r0 = t0 + (2 * wave) * 16 + (lane & 15), r1 = r0 + 16;
+    r0 = r0 < T ? r0 : 0;
+    r1 = r1 < T ? r1 : 0;
+    a0p = x + (size_t)r0 * H + kbeg + kl;
+    a1p = x + (size_t)r1 * H + kbeg + kl;
   }
+  const uint16_t* bp[3];
 #pragma unroll
-  for (int n = 0; n < NE; ++n) {
-    const int e = e0 + n * 16 + (lane & 15);
-    wrow[n] = wr + (size_t)(e < E ? e : 0) * H + kl;
+  for (int q = 0; q < 3; ++q) {
+    int e = e0 + (3 * wave + q) * 16 + (lane & 15);
+    e = (3 * wave + q < kRlBFrags && e < E) ? e : 0;
+    bp[q] = wr + (size_t)e * H + kbeg + kl;
   }
-  f32x4 acc[NT][NE];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int n = 0; n < NE; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 a0[NT], b0[NE], a1[NT], b1[NE];
-  auto load = [&](u32x4(&a)[NT], u32x4(&b)[NE], int k) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) a[t] = load16(xrow[t] + k);
-#pragma unroll
-    for (int n = 0; n < NE; ++n) b[n] = load16(wrow[n] + k);
+  auto issue = [&](int kk, int slot) {
+    uint8_t* st = lds + slot * kRlStage;
+    uint8_t* la = st + 2 * wave * kFragBytes;
+    load_frag<0>(a0p + (size_t)kk * 32, la);
+    load_frag<kFragBytes>(reinterpret_cast<const uint8_t*>(a1p + (size_t)kk * 32) - kFragBytes, la);
+    uint8_t* lb = st + (kRlAFrags + 3 * wave) * kFragBytes;
+    load_frag<0>(bp[0] + (size_t)kk * 32, lb);
+    load_frag<kFragBytes>(reinterpret_cast<const uint8_t*>(bp[1] + (size_t)kk * 32) - kFragBytes, lb);
+    load_frag<2 * kFragBytes>(
+        reinterpret_cast<const uint8_t*>(bp[2] + (size_t)kk * 32) - 2 * kFragBytes, lb);
   };
-  auto mma = [&](const u32x4(&a)[NT], const u32x4(&b)[NE]) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int n = 0; n < NE; ++n) acc[t][n] = mfma16(as_bf16x8(a[t]), as_bf16x8(b[n]), acc[t][n]);
+  auto rd_a = [&](int kk, int m) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + (kk % kRlStages) * kRlStage +
+                                                     (4 * wt + m) * kFragBytes + lane * 16));
   };
-  load(a0, b0, kbeg);
-  for (int k = kbeg; k < kend; k += 64) {
-    load(a1, b1, k + 32);
-    mma(a0, b0);
-    if (k + 64 < kend) load(a0, b0, k + 64);
-    mma(a1, b1);
-  }
-  float* dst = part + (size_t)blockIdx.z * T * E;
+  auto rd_b = [&](int kk, int j) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(
+        lds + (kk % kRlStages) * kRlStage + (kRlAFrags + 9 * we + j) * kFragBytes + lane * 16));
+  };
+
+  f32x4 acc[4][9];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < NE; ++n) {
-      const int e = e0 + n * 16 + (lane & 15);
-      if (e >= E) continue;
+    for (int j = 0; j < 9; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 a0[4], a1[4], b[9];
+  // step kk: wait for step kk+1's loads (own: vmcnt, everyone's: barrier),
+  // refill the slot of step kk (already in registers) with step kk+3, then
+  // the MFMAs of step kk while step kk+1 is read into registers
+  auto step = [&](int kk, bf16x8(&ca)[4], bf16x8(&na)[4], bool do_issue, bool do_read, int vm) {
+    wait_vm_lgkm0(vm);
+    barrier();
+    if (do_issue) issue(kk + kRlStages, kk % kRlStages);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + t * 16 + (lane >> 4) * 4 + i;
-        if (tok < T) dst[(size_t)tok * E + e] = acc[t][n][i];
+    for (int j = 0; j < 9; ++j) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[m][j] = mfma16(ca[m], b[j], acc[m][j]);
+      if (do_read) {
+        b[j] = rd_b(kk + 1, j);
+        if (j < 4) na[j] = rd_a(kk + 1, j);
       }
     }
+  };
+  const int pro = nk < kRlStages ? nk : kRlStages;
+  for (int s = 0; s < pro; ++s) issue(s, s);
+  wait_vm_lgkm0((pro - 1) * per_step);
+  barrier();
+#pragma unroll
+  for (int m = 0; m < 4; ++m) a0[m] = rd_a(0, m);
+#pragma unroll
+  for (int j = 0; j < 9; ++j) b[j] = rd_b(0, j);
+  // loads issued after step kk+1's that may still be in flight at step kk
+  auto vm_at = [&](int kk) { return kk + 2 < nk ? per_step : 0; };
+  int kk = 0;
+  for (; kk + kRlStages + 1 < nk; kk += 2) {
+    step(kk, a0, a1, true, true, per_step);
+    step(kk + 1, a1, a0, true, true, per_step);
+  }
+  for (; kk < nk; kk += 2) {
+    step(kk, a0, a1, kk + kRlStages < nk, kk + 1 < nk, vm_at(kk));
+    if (kk + 1 < nk) step(kk + 1, a1, a0, kk + 1 + kRlStages < nk, kk + 2 < nk, vm_at(kk + 1));
+  }
+
+  float* dst = part + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int e = e0 + (9 * we + j) * 16 + (lane & 15);
+    if (e >= E) continue;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 64 * wt + 16 * m + (lane >> 4) * 4 + i;
+        if (tok < T) dst[(size_t)tok * E + e] = acc[m][j][i];
+      }
+  }
 }
 
 // One wave per token.
@@ -217,27 +273,26 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 namespace {
 struct RouterShape {
   int nt, ne, nw;
-  bool wide;
+  bool lds;  // router_logits_lds_kernel
 };
-RouterShape router_shape(bool x_f32, int T, int ksteps) {
-  if (!x_f32 && T > 256 && ksteps % 2 == 0) return {4, 6, 3, true};
+RouterShape router_shape(bool x_f32, int T) {
+  if (!x_f32 && T > 256) return {kRlTokens / 16, kRlExperts / 16, 1, true};
   return {T <= 32 ? 2 : 4, 1, 1, false};
 }
 }  // namespace
 
 int router_blocks(bool x_f32, int T, int E) {
-  const RouterShape r = router_shape(x_f32, T, 2);
+  const RouterShape r = router_shape(x_f32, T);
   return ((T + 16 * r.nt - 1) / (16 * r.nt)) * ((E + 16 * r.ne * r.nw - 1) / (16 * r.ne * r.nw));
 }
 
 hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
                                 int T, int H, int E, int ks, int32_t* done, hipStream_t s) {
   const int kchunk = H / ks;
-  // the wide kernel takes an even number of 32-wide k-steps per slice
-  const RouterShape r = router_shape(x_f32, T, kchunk / 32);
+  const RouterShape r = router_shape(x_f32, T);
   dim3 grid((T + 16 * r.nt - 1) / (16 * r.nt), (E + 16 * r.ne * r.nw - 1) / (16 * r.ne * r.nw), ks);
-  if (r.wide) {
-    hipLaunchKernelGGL((router_logits_wide_kernel<4, 6, 3>), grid, dim3(64 * 3), 0, s,
+  if (r.lds) {
+    hipLaunchKernelGGL(router_logits_lds_kernel, grid, dim3(512), 0, s,
                        static_cast<const uint16_t*>(x), router_w, part, T, H, E, kchunk, done);
     return hipGetLastError();
   }
