@@ -1,5 +1,7 @@
-// Router: logits l = x W_r^T (+ b) in fp32, then per token a wave-level
-// softmax / sigmoid score, top-k selection and renormalisation.
+// Router: logits l = x W_r^T (+ b) in fp32, as K-slice partial sums; the
+// per-token softmax / sigmoid score, top-k selection and renormalisation
+// (moe_topk.hpp) run here for batches over 1024 tokens and inside the
+// dispatch launch below that.
 //
 // Source: llm-atlas "Step-3.5-Flash", table "Champs bruts du config.json"
 // (moe_num_experts, moe_top_k, norm_expert_weight, need_fp32_gate,
