@@ -192,6 +192,18 @@ def test_large_batch_dispatch(tokens, act):
     _run(s)
 
 
+@pytest.mark.parametrize("act,experts,tokens", [("bf16", 2, 3), ("f32", 2, 3), ("bf16", 1, 100),
+                                                ("bf16", 1, 200), ("bf16", 2, 300)])
+def test_minimal_widths(act, experts, tokens):
+    """The smallest widths the boundary accepts (hidden 64, expert widths 32):
+    one K step of the router and of the down GEMM, one double step of the
+    256-row gate/up tiles (200 rows on one expert), 128-row tiles (100 rows),
+    the LDS-staged router with a single K step (300 tokens)."""
+    s = W["tiny"].replace(name=f"minimal_{act}_{experts}_{tokens}", act_dtype=act, hidden=64,
+                          experts=experts, top_k=1, inter=32, shared_inter=32, tokens=tokens)
+    _run(s)
+
+
 @pytest.mark.parametrize("tokens", [64, 700])
 def test_max_experts_and_top_k(tokens):
     """The largest expert count and top-k the boundary accepts (512, 16): every
