@@ -10,12 +10,67 @@
 namespace moe {
 namespace {
 
-template <bool OUT_F32>
+// Small batches: one thread per 4 output columns of one token, a token's
+// row spread over ceil(H / 1024) workgroups.  The token's routing entries are
+// the same for every thread (scalar loads), and the thread issues the loads of
+// all KMAX >= k rows before any arithmetic (a loop over the rows would wait
+// for each row in turn): rows past k re-read row k-1 and are zeroed by a
+// select.  Y is read once: nontemporal loads keep it from displacing cached
+// data.
+template <bool OUT_F32, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int H,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int k, int P,
                                                       int has_shared, void* __restrict__ out,
                                                       int T) {
+  const int t = blockIdx.x;
+  const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+  if (t >= T || col >= H) return;
+  int rows[KMAX];
+  float wj[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int jj = j < k ? j : k - 1;
+    const int r = inv[(size_t)t * k + jj];
+    rows[j] = r < 0 ? 0 : (r >= P ? P - 1 : r);
+    wj[j] = w[(size_t)t * k + jj];
+  }
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // shared row (or, without a shared expert, any valid row, then zeroed)
+  const size_t srow = has_shared ? (size_t)(P + t) : (size_t)rows[0];
+  const f32x4 sh = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + srow * H + col));
+  f32x4 v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)rows[j] * H + col));
+  // fixed order: shared, then j = 0 .. k-1
+  f32x4 acc = has_shared ? sh : zero;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const f32x4 vj = j < k ? v[j] : zero;
+    const float cw = j < k ? wj[j] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += cw * vj[e];
+  }
+  if (OUT_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)t * H + col) = acc;
+  } else {
+    uint2 pk;
+    pk.x = pack_bf16x2(acc[0], acc[1]);
+    pk.y = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * H + col) = pk;
+  }
+}
+
+// Large batches: one workgroup per token, a thread owns 4 groups of 4
+// columns; the rows are walked in order, the 4 groups' loads of a row in
+// flight together, so each row is read as one contiguous run per workgroup.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ y, int H,
+                                                           const int32_t* __restrict__ inv,
+                                                           const float* __restrict__ w, int k,
+                                                           int P, int has_shared,
+                                                           void* __restrict__ out, int T) {
   const int t = blockIdx.x;
   if (t >= T) return;
   __shared__ int rows[kMaxTopK];
@@ -72,13 +127,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
                           int k, int P, int has_shared, void* out, int T, hipStream_t s) {
-  dim3 grid(T), block(256);
-  if (out_f32)
-    hipLaunchKernelGGL((combine_kernel<true>), grid, block, 0, s, y, H, inv, w, k, P, has_shared,
-                       out, T);
-  else
-    hipLaunchKernelGGL((combine_kernel<false>), grid, block, 0, s, y, H, inv, w, k, P, has_shared,
-                       out, T);
+  if (k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
+  if (T >= 512) {  // bandwidth-bound: whole rows per workgroup
+    dim3 grid(T), block(256);
+    if (out_f32)
+      hipLaunchKernelGGL((combine_rows_kernel<true>), grid, block, 0, s, y, H, inv, w, k, P,
+                         has_shared, out, T);
+    else
+      hipLaunchKernelGGL((combine_rows_kernel<false>), grid, block, 0, s, y, H, inv, w, k, P,
+                         has_shared, out, T);
+    return hipGetLastError();
+  }
+  dim3 grid(T, (H / 4 + 255) / 256), block(256);
+#define MOE_CB(F32, KM)                                                                          \
+  hipLaunchKernelGGL((combine_kernel<F32, KM>), grid, block, 0, s, y, H, inv, w, k, P, has_shared, \
+                     out, T)
+#define MOE_CB_K(F32)                   \
+  if (k <= 2) MOE_CB(F32, 2);           \
+  else if (k <= 4) MOE_CB(F32, 4);      \
+  else if (k <= 8) MOE_CB(F32, 8);      \
+  else MOE_CB(F32, 16)
+  if (out_f32) {
+    MOE_CB_K(true);
+  } else {
+    MOE_CB_K(false);
+  }
+#undef MOE_CB_K
+#undef MOE_CB
   return hipGetLastError();
 }
 
