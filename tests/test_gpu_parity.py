@@ -135,6 +135,33 @@ def test_deterministic():
     assert torch.equal(r1.perm, r2.perm) and torch.equal(r1.topk_idx, r2.topk_idx)
 
 
+def test_concurrent_streams_one_handle():
+    """Forwards on one handle, on two streams at once, each with its own
+    workspace and output, give bit for bit what each gives alone: a 32-token
+    batch (fused top-k + dispatch, streaming GEMMs) beside a 568-token one
+    (LDS-staged router, tiled GEMMs)."""
+    s = W["tiny"].replace(name="tiny_bf16_600", act_dtype="bf16", tokens=600)
+    inp = moe_synth.make_layer(s, seed=3, device="cuda")
+    layer = make_layer(s)
+    layer.pack_inputs(inp)
+    xa, xb = inp.x[:32].contiguous(), inp.x[32:].contiguous()
+    ref_a = layer.forward(xa, inp.router_w)
+    ref_b = layer.forward(xb, inp.router_w)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        ws_a = torch.empty(layer.workspace_bytes(32), dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(layer.workspace_bytes(xb.shape[0]), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            oa = layer.forward(xa, inp.router_w, workspace=ws_a)
+        with torch.cuda.stream(s2):
+            ob = layer.forward(xb, inp.router_w, workspace=ws_b)
+        torch.cuda.synchronize()
+        _say("concurrent", rep)
+        assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
+
+
 def test_argument_errors():
     from sparse_mixture_experts_layer_amd import _binding as B
     s = W["tiny"]
