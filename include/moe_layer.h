@@ -27,7 +27,8 @@
  *     buffer (activations, router weights, packed weights, output, workspace);
  *     the library allocates no device memory.  A handle owns host state only.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
- *     Nothing synchronises the host.
+ *     Nothing synchronises the host, and a forward enqueues kernels only (no
+ *     memset or copy nodes), so it can be captured in a HIP graph.
  *   - Argument errors are detected before anything is enqueued and returned as
  *     a status; moe_last_error() then holds a message (per thread).  Launch
  *     failures return MOE_ERR_DEVICE.  Faults inside kernels surface at the
