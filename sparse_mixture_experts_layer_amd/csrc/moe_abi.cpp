@@ -116,12 +116,16 @@ Plan make_plan(const moe_layer& L, int T) {
   const double rows_per_expert = (double)p.P / c.num_experts;
   p.tg = rows_per_expert < 2.0 ? 1 : (rows_per_expert < 24.0 ? 2 : 4);
   if (c.weight_dtype == MOE_INT4_G32 && p.tg > 2) p.tg = 2;  // register budget
-  // MFMA regime (64+ rows per expert): LDS-staged tiles with bf16 h (bf16
-  // weights and activations only)
-  p.tiled = rows_per_expert >= 64.0 && c.weight_dtype == MOE_BF16 && c.act_dtype == MOE_BF16;
-  // 256-row tiles (one 8-wave workgroup per CU) once experts hold ~200+ rows:
-  // fewer bytes pulled per flop, the bound of these GEMMs
-  if (p.tiled) p.tg = rows_per_expert >= 192.0 ? 16 : 8;
+  // LDS-staged tiles with bf16 h (bf16 weights and activations only) from 16
+  // rows per expert on: measured even at 16 rows and ahead from ~20 (4% at
+  // 21-28 rows, 10-28% at 36-57 rows, where the streaming kernels with
+  // 64-row groups run at two waves per SIMD)
+  p.tiled = rows_per_expert >= 16.0 && c.weight_dtype == MOE_BF16 && c.act_dtype == MOE_BF16;
+  // 256-row tiles (one 8-wave workgroup per CU) from 128 rows per expert:
+  // fewer bytes pulled per flop, the bound of these GEMMs (9-11% ahead at
+  // 142-178 rows), but a tile that is mostly padding below that (96-114
+  // rows: 128-row tiles 10% ahead)
+  if (p.tiled) p.tg = rows_per_expert >= 128.0 ? 16 : 8;
   const int bm = 16 * p.tg;
   const int nz = c.num_experts < p.P ? c.num_experts : p.P;
   p.max_tiles = nz + p.P / bm + (p.has_shared ? (T + bm - 1) / bm : 0) + 1;
