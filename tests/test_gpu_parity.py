@@ -217,7 +217,7 @@ TILED_SMALL = W["tiny"].replace(name="tiled_small", act_dtype="bf16", tokens=512
 
 @pytest.mark.parametrize("tokens", [512, 300, 1000])
 def test_tiled_small_ragged(tokens):
-    """64+ rows per expert selects the LDS-tiled GEMMs: partial 128-row tiles,
+    """16+ rows per expert selects the LDS-tiled GEMMs: partial 128-row tiles,
     intermediate width 64 (half a 256-row weight tile)."""
     _run(TILED_SMALL, tokens=tokens, max_tokens=1000)
 
