@@ -22,7 +22,7 @@
 namespace moe {
 namespace {
 
-// Small batches: a workgroup computes 16*NT tokens x 16 experts over one K
+// Up to 640 tokens (or fp32 x): a workgroup computes 16*NT tokens x 16 experts over one K
 // slice, which its 4 waves split in 4 and add up through LDS.  Tokens are the
 // MFMA A operand and router rows the B operand, so a lane ends with one expert
 // column of 4 token rows per token group.  At these sizes the kernel is a
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
     }
 }
 
-// Large batches, bf16 x: LDS-staged tiles of 256 tokens x 288 experts (all
+// Batches over 640 tokens, bf16 x: LDS-staged tiles of 256 tokens x 288 experts (all
 // of Step-3.5-Flash's router) over one K slice, so each router row is fetched
 // once per 256 tokens instead of once per 64.  8 waves, wave (wt, we) = (wave
 // % 4, wave / 4) owns tokens 64*wt .. +63 and experts 144*we .. +143 (4 x 9
@@ -278,7 +278,9 @@ struct RouterShape {
   bool lds;  // router_logits_lds_kernel
 };
 RouterShape router_shape(bool x_f32, int T) {
-  if (!x_f32 && T > 256) return {kRlTokens / 16, kRlExperts / 16, 1, true};
+  // the LDS-staged tiles pay off once a few of them fill the GPU: measured
+  // behind the small-batch kernel at 384-512 tokens, ahead from 1024
+  if (!x_f32 && T > 640) return {kRlTokens / 16, kRlExperts / 16, 1, true};
   return {T <= 32 ? 2 : 4, 1, 1, false};
 }
 }  // namespace

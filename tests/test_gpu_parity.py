@@ -138,9 +138,9 @@ def test_deterministic():
 def test_concurrent_streams_one_handle():
     """Forwards on one handle, on two streams at once, each with its own
     workspace and output, give bit for bit what each gives alone: a 32-token
-    batch (fused top-k + dispatch, streaming GEMMs) beside a 568-token one
+    batch (fused top-k + dispatch, streaming GEMMs) beside a 700-token one
     (LDS-staged router, tiled GEMMs)."""
-    s = W["tiny"].replace(name="tiny_bf16_600", act_dtype="bf16", tokens=600)
+    s = W["tiny"].replace(name="tiny_bf16_732", act_dtype="bf16", tokens=732)
     inp = moe_synth.make_layer(s, seed=3, device="cuda")
     layer = make_layer(s)
     layer.pack_inputs(inp)
@@ -253,12 +253,12 @@ def test_large_batch_dispatch(tokens, act):
 
 
 @pytest.mark.parametrize("act,experts,tokens", [("bf16", 2, 3), ("f32", 2, 3), ("bf16", 1, 100),
-                                                ("bf16", 1, 200), ("bf16", 2, 300)])
+                                                ("bf16", 1, 200), ("bf16", 2, 700)])
 def test_minimal_widths(act, experts, tokens):
     """The smallest widths the boundary accepts (hidden 64, expert widths 32):
     one K step of the router and of the down GEMM, one double step of the
     256-row gate/up tiles (200 rows on one expert), 128-row tiles (100 rows),
-    the LDS-staged router with a single K step (300 tokens)."""
+    the LDS-staged router with a single K step (700 tokens)."""
     s = W["tiny"].replace(name=f"minimal_{act}_{experts}_{tokens}", act_dtype=act, hidden=64,
                           experts=experts, top_k=1, inter=32, shared_inter=32, tokens=tokens)
     _run(s)
@@ -308,10 +308,10 @@ def test_decode_ragged(tokens):
 @pytest.mark.parametrize("tokens", [128, 257, 1024, 1025])
 def test_mid_size_batches_sampled(tokens):
     """Batch sizes between decode and prefill at the full layer shape: 128
-    (2 token groups per tile), 257 (first size on the wide router kernel and
-    on 16-token top-k + dispatch workgroups), 1024 (last size of the fused
-    top-k + dispatch: 64 tokens per dispatching wave), 1025 (first size on
-    the multi-workgroup dispatch, 4 token groups)."""
+    (2 token groups per tile), 257 (first size on 16-token top-k + dispatch
+    workgroups), 1024 (LDS-staged router; last size of the fused top-k +
+    dispatch: 64 tokens per dispatching wave), 1025 (first size on the
+    multi-workgroup dispatch)."""
     s = W["decode"].replace(name=f"mid_{tokens}", tokens=tokens)
     _run(s, sample=_spread(tokens, 10))
 
