@@ -96,10 +96,17 @@ moe_status_t check_config(const moe_layer_config_t* c) {
 // Per-call plan and workspace layout.
 struct Plan {
   int T, P, ks, tg, max_tiles, has_shared, hstride, tiled;
-  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, done, blk_hist, h,
-      h_lo, y, total;
+  // hybrid: streaming GEMMs for most groups, LDS-tiled ones (tg2, list 2) for
+  // the groups with `hot` rows or more
+  int hybrid, hot, tg2, max_tiles2;
+  size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, tiles2, ntiles2,
+      done, blk_hist, h, h_lo, h2, y, total;
   int large_dispatch;
 };
+
+// Rows from which a group leaves the streaming GEMMs for the LDS-tiled ones
+// in a load-imbalanced batch.
+constexpr int kHotRows = 32;
 
 Plan make_plan(const moe_layer& L, int T) {
   const moe_layer_config_t& c = L.cfg;
@@ -126,9 +133,26 @@ Plan make_plan(const moe_layer& L, int T) {
   // 142-178 rows), but a tile that is mostly padding below that (96-114
   // rows: 128-row tiles 10% ahead)
   if (p.tiled) p.tg = rows_per_expert >= 128.0 ? 16 : 8;
+  // one workgroup dispatches small batches; larger ones use per-block counts
+  p.large_dispatch = T > 1024;
+  // Streaming batches whose routing is uneven (a Zipf-popular expert can
+  // take most of the tokens) would stream a hot expert's weights once per
+  // 16-32-row tile: routed experts with kHotRows rows or more go to 128-row
+  // LDS tiles instead, in a launch after the streaming one.  The shared
+  // expert stays with the streaming GEMMs (a launch of its tiles alone would
+  // occupy a handful of CUs).  From 256 tokens: with Zipf-popular experts
+  // measured 6% faster at 256 tokens and 12% at 512, but 5% slower at 128,
+  // where the hot experts' few tiles leave the extra launch mostly idle;
+  // neutral on uniform routing.
+  p.hybrid = !p.tiled && !p.large_dispatch && c.weight_dtype == MOE_BF16 &&
+             c.act_dtype == MOE_BF16 && T >= 256;
+  p.hot = p.hybrid ? kHotRows : 0;
+  p.tg2 = 8;
   const int bm = 16 * p.tg;
   const int nz = c.num_experts < p.P ? c.num_experts : p.P;
   p.max_tiles = nz + p.P / bm + (p.has_shared ? (T + bm - 1) / bm : 0) + 1;
+  // list 2: at most P / kHotRows routed groups, ceil(rows / 128) tiles each
+  p.max_tiles2 = p.hybrid ? p.P / (16 * p.tg2) + p.P / kHotRows + 1 : 0;
   const int rows = p.P + (p.has_shared ? T : 0);
   p.hstride = c.inter > c.shared_inter ? c.inter : c.shared_inter;
   const int E = c.num_experts;
@@ -150,9 +174,9 @@ Plan make_plan(const moe_layer& L, int T) {
   p.row_tok = take((size_t)rows * 4);
   p.tiles = take((size_t)p.max_tiles * 4);
   p.ntiles = take(4);
+  p.tiles2 = take((size_t)p.max_tiles2 * 4);
+  p.ntiles2 = take(p.hybrid ? 4 : 0);
   p.done = take(4);
-  // one workgroup dispatches small batches; larger ones use per-block counts
-  p.large_dispatch = T > 1024;
   p.blk_hist = take(p.large_dispatch ? (size_t)moe::dispatch_blocks(T) * E * 4 : 0);
   // h: fp32 rows on the streaming bf16 path; bf16 in packed fragment order,
   // with a 16-row gap per group and a tile of slack, on the tiled path
@@ -163,6 +187,8 @@ Plan make_plan(const moe_layer& L, int T) {
   p.h_lo = take(!lo_plane ? 0
                 : p.tiled ? moe::tiled_h_rows(T, 0) * p.hstride * 2
                           : (size_t)T * p.hstride * 2);
+  // the hybrid's LDS-tiled groups (routed only): packed h of their own
+  p.h2 = take(p.hybrid ? h_rows_tiled * p.hstride * 2 : 0);
   p.y = take((size_t)rows * c.hidden * 4);
   p.total = o;
   return p;
@@ -365,11 +391,13 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
                                      perm, inv, row_tok, tiles, ntiles, stream);
   } else {
     if (e == hipSuccess) e = mark(1);
+    const moe::TileLists tl{16 * p.tg, p.hot, 16 * p.tg2, tiles, ntiles,
+                            p.hybrid ? reinterpret_cast<int32_t*>(ws + p.tiles2) : nullptr,
+                            p.hybrid ? reinterpret_cast<int32_t*>(ws + p.ntiles2) : nullptr};
     if (e == hipSuccess)
       e = moe::launch_topk_dispatch(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
                                     c.renormalize, c.routed_scale, idx, wts, gap, done,
-                                    p.has_shared, 16 * p.tg, counts, offsets, perm, inv, row_tok,
-                                    tiles, ntiles, stream);
+                                    p.has_shared, tl, counts, offsets, perm, inv, row_tok, stream);
   }
   if (e == hipSuccess) e = mark(2);
   moe::GemmGeom g{};
@@ -386,8 +414,16 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g.counts = counts;
   g.max_tiles = p.max_tiles;
   g.tg = p.tg;
+  // the shared group's tiles close list 1
+  g.shared_tiles = p.has_shared ? (T + 16 * p.tg - 1) / (16 * p.tg) : 0;
   g.limit = c.swiglu_limit;
   g.limit_shared = c.swiglu_limit_shared;
+  moe::GemmGeom g2 = g;  // the hybrid's LDS-tiled groups
+  g2.tiles = reinterpret_cast<int32_t*>(ws + p.tiles2);
+  g2.ntiles = reinterpret_cast<int32_t*>(ws + p.ntiles2);
+  g2.max_tiles = p.max_tiles2;
+  g2.tg = p.tg2;
+  g2.shared_tiles = 0;
   if (p.tiled) {
     uint16_t* hb = reinterpret_cast<uint16_t*>(h);
     uint16_t* hl = reinterpret_cast<uint16_t*>(ws + p.h_lo);
@@ -398,10 +434,16 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     if (e == hipSuccess) e = moe::launch_down_tiled(g, hb, hl, p.hstride, y, stream);
   } else {
     uint16_t* hl = reinterpret_cast<uint16_t*>(ws + p.h_lo);
+    uint16_t* h2 = reinterpret_cast<uint16_t*>(ws + p.h2);
     if (e == hipSuccess)
       e = moe::launch_gateup(g, int4, f32, x, row_tok, h, hl, p.hstride, stream);
+    if (e == hipSuccess && p.hybrid)
+      e = moe::launch_gateup_tiled(g2, static_cast<const uint16_t*>(x), row_tok, h2, nullptr,
+                                   p.hstride, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = moe::launch_down(g, int4, f32, h, hl, p.hstride, y, stream);
+    if (e == hipSuccess && p.hybrid)
+      e = moe::launch_down_tiled(g2, h2, nullptr, p.hstride, y, stream);
   }
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)

@@ -60,16 +60,16 @@ __device__ int block_exclusive_scan(int* buf, int* total_slot, int n) {
 // waves (the last one of the top-k + dispatch kernel).
 template <int NW>
 __device__ __forceinline__ void dispatch_body(
-    const int32_t* __restrict__ idx, int T, int k, int E, int has_shared, int bm,
+    const int32_t* __restrict__ idx, int T, int k, int E, int has_shared, TileLists lists,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ row_tok, int32_t* __restrict__ tiles,
-    int32_t* __restrict__ ntiles_out) {
+    int32_t* __restrict__ inv, int32_t* __restrict__ row_tok) {
   constexpr int NTH = NW * kWave;
   __shared__ int hist[NW][kMaxExperts];                 // 2 KiB per wave
   __shared__ unsigned long long mask[NW][kMaxExperts];  // 4 KiB per wave
   __shared__ int tot[kMaxExperts + 1];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int ntile[kMaxExperts + 1];
+  __shared__ int ntile2[kMaxExperts + 1];
   __shared__ int scan_total;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -121,26 +121,40 @@ __device__ __forceinline__ void dispatch_body(
   for (int ex = tid; ex < E; ex += NTH) {
     counts[ex] = tot[ex];
     offsets[ex] = off[ex];
-    ntile[ex] = (tot[ex] + bm - 1) / bm;
     for (int w = 0; w < NW; ++w) hist[w][ex] += off[ex];
   }
   if (tid == 0) {
     counts[E] = has_shared ? T : 0;
     offsets[E] = P;
     offsets[E + 1] = P + (has_shared ? T : 0);
-    ntile[E] = has_shared ? (T + bm - 1) / bm : 0;
+  }
+  // tile counts per group and list
+  for (int gr = tid; gr <= E; gr += NTH) {
+    const int c = gr < E ? tot[gr] : (has_shared ? T : 0);
+    const bool second = gr < E && lists.in_second(c);
+    ntile[gr] = second ? 0 : (c + lists.bm - 1) / lists.bm;
+    ntile2[gr] = second ? (c + lists.bm2 - 1) / lists.bm2 : 0;
   }
   __syncthreads();
 
-  // tile list: groups in order 0..E, m-tiles in order inside a group
+  // tile lists: groups in order 0..E, m-tiles in order inside a group
   const int total_tiles = block_exclusive_scan(ntile, &scan_total, E + 1);
-  // ntile[] now holds each group's first tile; the tile count is recomputed.
+  const int total_tiles2 = lists.hot > 0 ? block_exclusive_scan(ntile2, &scan_total, E + 1) : 0;
+  // ntile[] / ntile2[] now hold each group's first tile; the counts are recomputed
   for (int gr = tid; gr <= E; gr += NTH) {
     const int c = gr < E ? tot[gr] : (has_shared ? T : 0);
-    const int nt = (c + bm - 1) / bm;
-    for (int m = 0; m < nt; ++m) tiles[ntile[gr] + m] = (gr << 16) | m;
+    if (gr < E && lists.in_second(c)) {
+      const int nt = (c + lists.bm2 - 1) / lists.bm2;
+      for (int m = 0; m < nt; ++m) lists.tiles2[ntile2[gr] + m] = (gr << 16) | m;
+    } else {
+      const int nt = (c + lists.bm - 1) / lists.bm;
+      for (int m = 0; m < nt; ++m) lists.tiles[ntile[gr] + m] = (gr << 16) | m;
+    }
   }
-  if (tid == 0) ntiles_out[0] = total_tiles;
+  if (tid == 0) {
+    lists.ntiles[0] = total_tiles;
+    if (lists.hot > 0) lists.ntiles2[0] = total_tiles2;
+  }
 
   // 3. stable scatter: a pair's row = the wave's first row of its expert +
   // the lanes below holding that expert (a token holds an expert once)
@@ -182,9 +196,8 @@ __global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
     const float* __restrict__ part, int ks, const float* __restrict__ bias, int bias_mode, int T,
     int E, int k, int score, int renorm, float scale, int32_t* __restrict__ idx,
     float* __restrict__ wout, float* __restrict__ gap, int32_t* __restrict__ done,
-    int has_shared, int bm, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_tok,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles_out) {
+    int has_shared, TileLists lists, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_tok) {
   __shared__ int last;
   const int t = blockIdx.x * NW + (threadIdx.x >> 6);
   if (t < T) topk_token(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
@@ -198,8 +211,7 @@ __global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
   }
   __syncthreads();
   if (!last) return;
-  dispatch_body<NW>(idx, T, k, E, has_shared, bm, counts, offsets, perm, inv, row_tok, tiles,
-                    ntiles_out);
+  dispatch_body<NW>(idx, T, k, E, has_shared, lists, counts, offsets, perm, inv, row_tok);
 }
 
 // ---------------------------------------------------------------- large batches
@@ -363,16 +375,18 @@ hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int ha
 
 hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, int bias_mode, int T,
                                 int E, int k, int score, int renorm, float scale, int32_t* idx,
-                                float* w, float* gap, int32_t* done, int has_shared, int bm,
-                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                                int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s) {
+                                float* w, float* gap, int32_t* done, int has_shared,
+                                const TileLists& tl, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, int32_t* row_tok, hipStream_t s) {
   if (T < 1 || T > kDispThreads || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
+  if (tl.bm < 1 || (tl.hot > 0 && (tl.bm2 < 1 || !tl.tiles2 || !tl.ntiles2)))
+    return hipErrorInvalidValue;
   // 4 tokens per workgroup up to 256 tokens (the top-k waves spread over more
   // CUs), 16 above
 #define MOE_TD(NW)                                                                              \
   hipLaunchKernelGGL(topk_dispatch_kernel<NW>, dim3((T + NW - 1) / NW), dim3(NW * 64), 0, s,  \
                      part, ks, bias, bias_mode, T, E, k, score, renorm, scale, idx, w, gap, done, \
-                     has_shared, bm, counts, offsets, perm, inv, row_tok, tiles, ntiles)
+                     has_shared, tl, counts, offsets, perm, inv, row_tok)
   if (T <= 4 * kWave) MOE_TD(4);
   else MOE_TD(kDispWaves);
 #undef MOE_TD

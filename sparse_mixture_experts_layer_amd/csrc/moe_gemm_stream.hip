@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
   constexpr bool SPLIT = AF32;            // fp32 A rows always enter as hi + lo
   constexpr bool LO = MODE == 1 && (HM == 2 || HM == 3);  // h_lo operand compiled in
   // down with HM 2 walks the shared group's tiles only (the last ones of the list)
-  const int nsh = MODE == 1 && HM == 2 ? (g.T + 16 * TG - 1) / (16 * TG) : 0;
+  const int nsh = MODE == 1 && HM == 2 ? g.shared_tiles : 0;
   const int tile = nsh ? *g.ntiles - nsh + (int)(blockIdx.x / nblk) : (int)(blockIdx.x / nblk);
   const int nb = blockIdx.x % nblk;
   TileInfo ti;
@@ -457,7 +457,7 @@ hipError_t launch_mode(const GemmGeom& g, bool int4, bool act_f32, const void* a
     // waves per SIMD measured slightly faster there)
     const bool even = (g.I / 32) % 2 == 0 && (g.Is / 32) % 2 == 0;
     const bool quad = (g.I / 32) % 4 == 0 && (g.Is / 32) % 4 == 0;
-    const int nsh = g.Is > 0 ? (g.T + 16 * TG - 1) / (16 * TG) : 0;
+    const int nsh = g.shared_tiles;
     dim3 grid_sh((unsigned)nsh * nblk);
     if (act_f32) {
       if (even) MOE_L(grid, MODE, false, TG, 2, 0);

@@ -19,15 +19,26 @@ hipError_t launch_router_topk(const float* part, int ks, const float* bias, int 
 
 // ---- dispatch: counts, offsets, stable permutation, GEMM tile list ----------
 // counts/offsets have E+1 / E+2 entries (group E = shared expert, T rows).
+// GEMM tile lists written by the dispatch: a routed expert with fewer than
+// `hot` rows goes to list 1 in tiles of bm rows, one with `hot` rows or more
+// to list 2 in tiles of bm2 rows; the shared expert (group E) always to list
+// 1, last; hot == 0 puts every group in list 1 (list 2 is then neither used
+// nor written).
+struct TileLists {
+  int bm, hot, bm2;
+  int32_t *tiles, *ntiles, *tiles2, *ntiles2;
+  __host__ __device__ bool in_second(int rows) const { return hot > 0 && rows >= hot; }
+};
+
 // Top-k (as launch_router_topk) and the dispatch in one launch, T <= 1024:
 // the last workgroup to finish its tokens' top-k runs the dispatch as one
 // workgroup.  done is a device counter that must read 0 at launch
 // (launch_router_logits clears it).
 hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, int bias_mode, int T,
                                 int E, int k, int score, int renorm, float scale, int32_t* idx,
-                                float* w, float* gap, int32_t* done, int has_shared, int bm,
-                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                                int32_t* row_tok, int32_t* tiles, int32_t* ntiles, hipStream_t s);
+                                float* w, float* gap, int32_t* done, int has_shared,
+                                const TileLists& tl, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, int32_t* row_tok, hipStream_t s);
 
 // Multi-workgroup variant for large batches (same outputs); blk_hist is
 // scratch of dispatch_blocks(T) * E int32.
@@ -48,6 +59,7 @@ struct GemmGeom {
   const int32_t* counts;      // [E+1] rows of each group
   int max_tiles;              // grid bound
   int tg;                     // token groups of 16 per tile (tile rows = 16 * tg)
+  int shared_tiles;           // tiles of the shared group at the end of this list (0: none)
   float limit, limit_shared;  // SwiGLU limits of the routed / shared experts (0 = none)
 };
 

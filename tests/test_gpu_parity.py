@@ -242,6 +242,28 @@ def test_tiled_many_rows_per_expert(tokens, inter, shared_inter):
     _run(s)
 
 
+@pytest.mark.parametrize("shared_inter", [64, 0])
+def test_hot_experts_take_tiles(shared_inter):
+    """A load-imbalanced streaming batch: a router bias sends most tokens to
+    three of 64 experts, which (with 32+ rows) go to the LDS-tiled GEMMs in
+    128-row tiles while the other experts (and the shared one) stream.
+    Compared on every token."""
+    s = W["tiny"].replace(name=f"hot_experts_{shared_inter}", act_dtype="bf16", experts=64,
+                          top_k=2, tokens=256, shared_inter=shared_inter)
+    inp = moe_synth.make_layer(s, seed=6, device="cuda")
+    bias = torch.zeros(s.experts, device="cuda", dtype=torch.float32)
+    bias[:3] = 3.0
+    inp.router_bias = bias
+    _say(s.name)
+    layer = make_layer(s)
+    layer.pack_inputs(inp)
+    out, route = run_gpu(layer, inp)
+    counts = route.expert_counts.cpu().numpy()
+    assert (counts[:3] >= 32).all() and (counts[3:] < 32).all(), counts
+    res = compare(inp, out, route, strict=False)
+    _say("ok", res)
+
+
 @pytest.mark.parametrize("tokens,act", [(3001, "bf16"), (1537, "f32")])
 def test_large_batch_dispatch(tokens, act):
     """Past 1024 tokens the dispatch runs over many workgroups (per-block
