@@ -162,28 +162,35 @@ def test_concurrent_streams_one_handle():
         assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
 
 
-@pytest.mark.parametrize("tokens", [32, 600])
-def test_graph_capture_replays(tokens):
+@pytest.mark.parametrize("tokens,experts", [(32, 16), (600, 16), (256, 64)])
+def test_graph_capture_replays(tokens, experts):
     """A forward captured in a HIP graph (no host synchronisation, no memset
     nodes: the fused dispatch's counter is cleared by a kernel) replays to the
-    eager result bit for bit, with other eager forwards in between."""
-    s = W["tiny"].replace(name=f"tiny_bf16_graph_{tokens}", act_dtype="bf16", tokens=tokens)
+    eager result bit for bit, with other eager forwards in between: streaming
+    GEMMs, LDS-tiled GEMMs, and streaming with hot experts on a second tile
+    list (a router bias makes three of 64 experts hot)."""
+    s = W["tiny"].replace(name=f"tiny_bf16_graph_{tokens}", act_dtype="bf16", tokens=tokens,
+                          experts=experts)
     inp = moe_synth.make_layer(s, seed=4, device="cuda")
+    bias = None
+    if experts == 64:
+        bias = torch.zeros(experts, device="cuda", dtype=torch.float32)
+        bias[:3] = 3.0
     layer = make_layer(s)
     layer.pack_inputs(inp)
     x = inp.x.clone()
-    ref = layer.forward(x, inp.router_w)
+    ref = layer.forward(x, inp.router_w, bias)
     out = torch.empty_like(ref)
     ws = torch.empty(layer.workspace_bytes(tokens), dtype=torch.uint8, device="cuda")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):          # warm-up off the capture
-        layer.forward(x, inp.router_w, out=out, workspace=ws)
+        layer.forward(x, inp.router_w, bias, out=out, workspace=ws)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        layer.forward(x, inp.router_w, out=out, workspace=ws)
+        layer.forward(x, inp.router_w, bias, out=out, workspace=ws)
     other = torch.flip(inp.x, dims=[0]).contiguous()
     for rep in range(4):
         out.zero_()
@@ -191,7 +198,7 @@ def test_graph_capture_replays(tokens):
         torch.cuda.synchronize()
         _say("graph replay", rep)
         assert torch.equal(out, ref)
-        layer.forward(other, inp.router_w)   # eager work between replays
+        layer.forward(other, inp.router_w, bias)   # eager work between replays
         torch.cuda.synchronize()
 
 
