@@ -99,15 +99,26 @@ def check(status: int, where: str) -> None:
         raise MoeError(status, where, last_error())
 
 
+# hip_runtime_api.h: an event that skips the system-scope fence of its record
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class StageEvents:
     """Sets of MOE_STAGE_EVENTS HIP events for moe_layer_forward_timed (one set
     per call, so back-to-back calls can be read afterwards), created and read
-    through the HIP runtime the process already loaded (torch's)."""
+    through the HIP runtime the process already loaded (torch's).
+
+    The events only time the stages: they are created with
+    hipEventDisableSystemFence, so recording one does not write back and
+    invalidate the caches (with default events the six records of a decode
+    step add ~20 us to it, with these ~10 us).  Waiting on one therefore says
+    nothing about the visibility of the layer's outputs; synchronise the
+    stream or device before reading them."""
 
     def __init__(self, sets: int = 1):
         load()
         self.hip = C.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
         self.hip.hipEventDestroy.argtypes = [C.c_void_p]
@@ -115,8 +126,8 @@ class StageEvents:
         self.array = (C.c_void_p * (MOE_STAGE_EVENTS * sets))()
         for i in range(MOE_STAGE_EVENTS * sets):
             ev = C.c_void_p()
-            if self.hip.hipEventCreate(C.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(C.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.array[i] = ev
 
     def ptr(self, s: int = 0) -> int:

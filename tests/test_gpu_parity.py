@@ -202,6 +202,28 @@ def test_graph_capture_replays(tokens, experts):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("tokens", [32, 1500])
+def test_timed_forward_matches(tokens):
+    """The timed entry point runs the same kernels as the plain one (same
+    output bit for bit) and leaves five finite, positive stage durations, on a
+    fused-dispatch batch and on one with the multi-workgroup dispatch."""
+    from sparse_mixture_experts_layer_amd import _binding as B
+    s = W["tiny"].replace(name=f"tiny_bf16_timed_{tokens}", act_dtype="bf16", tokens=tokens)
+    inp = moe_synth.make_layer(s, seed=6, device="cuda")
+    layer = make_layer(s)
+    layer.pack_inputs(inp)
+    ref = layer.forward(inp.x, inp.router_w)
+    ev = B.StageEvents(sets=2)
+    outs = [layer.forward(inp.x, inp.router_w, stage_events=ev, event_set=i) for i in range(2)]
+    torch.cuda.synchronize()
+    _say("timed forward", tokens)
+    for i, out in enumerate(outs):
+        assert torch.equal(out, ref)
+        ms = ev.stage_ms(i)
+        assert len(ms) == len(B.STAGES) == 5
+        assert all(np.isfinite(v) and v > 0 for v in ms), ms
+
+
 def test_argument_errors():
     from sparse_mixture_experts_layer_amd import _binding as B
     s = W["tiny"]
