@@ -271,6 +271,19 @@ def test_tiled_many_rows_per_expert(tokens, inter, shared_inter):
     _run(s)
 
 
+@pytest.mark.parametrize("tokens,hidden,inter,shared_inter,experts,top_k",
+                         [(8192, 256, 1024, 1024, 8, 2), (16000, 512, 96, 160, 8, 2),
+                          (16000, 256, 384, 0, 64, 2)])
+def test_tiled_256_many_tiles(tokens, hidden, inter, shared_inter, experts, top_k):
+    """256-row gate/up and down tiles with more tiles than CUs (several per
+    CU): the shortest K of these shapes (hidden 256: 8 k-steps) and a longer
+    one, ragged row tails, a partial column tile, a shared expert of another
+    width, no shared expert.  Compared on every token."""
+    s = TILED_SMALL.replace(name=f"tiled_256_{tokens}_{hidden}", experts=experts, top_k=top_k,
+                            hidden=hidden, inter=inter, shared_inter=shared_inter, tokens=tokens)
+    _run(s)
+
+
 @pytest.mark.parametrize("shared_inter", [64, 0])
 def test_hot_experts_take_tiles(shared_inter):
     """A load-imbalanced streaming batch: a router bias sends most tokens to
