@@ -26,7 +26,9 @@
  *   - Device pointers must be 16-byte aligned.  The caller owns every device
  *     buffer (activations, router weights, packed weights, output, workspace);
  *     the library allocates no device memory.  A handle owns host state only.
- *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream),
+ *     which must belong to the handle's device (the call makes that device
+ *     current while it enqueues and restores the caller's afterwards).
  *     Nothing synchronises the host, and a forward enqueues kernels only (no
  *     memset or copy nodes), so it can be captured in a HIP graph.
  *   - Argument errors are detected before anything is enqueued and returned as

@@ -17,6 +17,7 @@ MOE_F32, MOE_BF16, MOE_INT4_G32 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_STAGE_EVENTS = 6
+MOE_ABI_VERSION = 2     # the header these declarations follow
 STAGES = ("router", "dispatch", "gate_up", "down", "combine")
 
 
@@ -61,6 +62,10 @@ def load() -> C.CDLL:
     lib = C.CDLL(LIB_PATH)
     lib.moe_abi_version.restype = C.c_int
     lib.moe_abi_version.argtypes = []
+    if lib.moe_abi_version() != MOE_ABI_VERSION:   # struct layouts below would not match
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.moe_abi_version()}, these bindings "
+                           f"expect {MOE_ABI_VERSION} (rebuild: python -m "
+                           "sparse_mixture_experts_layer_amd.build)")
     lib.moe_layer_create.restype = C.c_int
     lib.moe_layer_create.argtypes = [C.POINTER(MoeLayerConfig), C.c_int, C.POINTER(C.c_void_p)]
     lib.moe_layer_destroy.restype = None

@@ -33,6 +33,16 @@ def _need(t: torch.Tensor, name: str, dtype, shape, device) -> None:
         raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
+def _need_bytes(t: torch.Tensor, name: str, min_bytes: int, device) -> None:
+    """A device byte buffer: contiguous uint8 of at least min_bytes."""
+    if t.dtype != torch.uint8 or t.dim() != 1 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous 1-D torch.uint8 tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.numel() < min_bytes:
+        raise ValueError(f"{name} has {t.numel()} bytes, {min_bytes} needed")
+
+
 @dataclass
 class Route:
     """Routing results of one forward (views into the workspace)."""
@@ -175,12 +185,15 @@ class MoELayer:
         packed = self.packed if packed is None else packed
         if packed is None:
             raise RuntimeError("weights are not packed (call pack first)")
+        _need_bytes(packed, "packed", self.packed_bytes, dev)
         if out is None:
             out = torch.empty((T, c.hidden), dtype=self.act_dtype, device=dev)
         else:
             _need(out, "out", self.act_dtype, (T, c.hidden), dev)
         if workspace is None:
             workspace = torch.empty(max(self.workspace_bytes(T), 1), dtype=torch.uint8, device=dev)
+        else:   # its size is checked by the library against the batch's plan
+            _need_bytes(workspace, "workspace", 0, dev)
         route = B.MoeRoute()
         args = (self._h, T, x.data_ptr(), router_w.data_ptr(), _ptr(router_bias),
                 packed.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(),

@@ -30,7 +30,11 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 2
+    """The header's version, the library's and the bindings' agree (the
+    bindings refuse a library of another version: its structs differ)."""
+    from sparse_mixture_experts_layer_amd import _binding as B
+    m = re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.moe_abi_version() == int(m.group(1)) == B.MOE_ABI_VERSION == 2
 
 
 def _cfg(**kw):
