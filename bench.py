@@ -32,10 +32,13 @@ PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E (published)
 PEAK_BF16 = 2.5e15         # flop/s, MI355X dense bf16 MFMA (published)
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_layer_amd", "csrc")
-# source of the dominant (gate/up) kernel per workload: LDS-tiled GEMMs for the
-# prefill batch, weight-streaming GEMMs for the decode-sized ones
-GEMM_SRC = {"prefill": os.path.join(CSRC, "moe_gemm_tiled.hip")}
-GEMM_SRC_DEFAULT = os.path.join(CSRC, "moe_gemm_stream.hip")
+# sources of the gate/up stage's kernels per workload: LDS-tiled GEMMs for the
+# prefill batch, weight-streaming GEMMs for the decode-sized ones, both for the
+# Zipf verify batch (its hot experts take LDS tiles)
+_STREAM = os.path.join(CSRC, "moe_gemm_stream.hip")
+_TILED = os.path.join(CSRC, "moe_gemm_tiled.hip")
+GEMM_SRC = {"prefill": [_TILED], "verify": [_STREAM, _TILED]}
+GEMM_SRC_DEFAULT = [_STREAM]
 
 
 def log(*a):
@@ -65,12 +68,13 @@ def src_digest(path: str) -> str:
 
 
 def read_counters(workload: str):
-    """HBM traffic of the gate/up kernel from committed rocprofv3 --pmc runs.
+    """HBM traffic of the gate/up stage from committed rocprofv3 --pmc runs.
 
     profiles/gate_up_<workload>_counters.txt holds 'key: value' lines, among
-    them src_sha (digest of the kernel source the counters were taken on) and
-    fetch_bytes / write_bytes per launch already scaled by the copy-kernel
-    calibration.  Returns None when absent or taken on other kernel code."""
+    them src_sha (digests of the kernel sources the counters were taken on,
+    comma-separated in GEMM_SRC order) and fetch_bytes / write_bytes per call
+    already scaled by the copy-kernel calibration.  Returns None when absent
+    or taken on other kernel code."""
     path = os.path.join(PROFILES, f"gate_up_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -79,7 +83,7 @@ def read_counters(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("src_sha") != src_digest(GEMM_SRC.get(workload, GEMM_SRC_DEFAULT)):
+    if kv.get("src_sha") != ",".join(src_digest(p) for p in GEMM_SRC.get(workload, GEMM_SRC_DEFAULT)):
         return None
     try:
         return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
