@@ -37,6 +37,19 @@
  *     caller's next synchronisation.
  *   - A handle is immutable after moe_layer_create: concurrent forwards on one
  *     handle are allowed when each uses its own workspace and output.
+ *   - A handle whose configuration has bf16 weights and activations and
+ *     max_tokens >= 256 owns a second stream (default priority, non-blocking),
+ *     created with it and destroyed by moe_layer_destroy.  Batches of 256 to
+ *     1024 tokens that take the streaming GEMMs put the hot experts' LDS-tiled
+ *     GEMMs there (few, long-running workgroups; a load-imbalanced batch has
+ *     them): forked from `stream` by an event after the dispatch and joined
+ *     back before the combine, so they overlap the streaming GEMMs on
+ *     `stream`.  The output is the same as with everything in order.
+ *     Concurrent forwards on one
+ *     handle share that stream (and serialise there); while a forward on a
+ *     handle is being captured into a graph, the second stream is part of the
+ *     capture, so no other forward on that handle may run until the capture
+ *     ends.
  */
 #ifndef MOE_LAYER_H
 #define MOE_LAYER_H
@@ -184,7 +197,9 @@ moe_status_t moe_layer_forward(moe_layer_t layer, int32_t num_tokens, const void
  * hipEventElapsedTime(stage_events[i], stage_events[i+1]) is the duration of
  * stage i.  Top-k selection runs in one launch with the dispatch for batches
  * of up to 1024 tokens (it is then timed in the dispatch stage) and with the
- * router logits above that.  stage_events holds MOE_STAGE_EVENTS events created by the caller
+ * router logits above that.  Work on the handle's second stream is timed only
+ * where `stream` waits for it, before the combine stage.  stage_events holds
+ * MOE_STAGE_EVENTS events created by the caller
  * (hipEventCreate or hipEventCreateWithFlags; events made with
  * hipEventDisableSystemFence only time the stages and skip the cache write-back
  * a default event's record performs, about 2 us each on a decode batch); the

@@ -46,6 +46,10 @@ struct moe_layer {
   int device;
   size_t expert_bytes;   // one routed expert, packed
   size_t shared_bytes;   // the shared expert, packed
+  // second stream (default priority, non-blocking) for the hot experts'
+  // LDS-tiled GEMMs, which then overlap the streaming GEMMs; created with the
+  // handle when its configuration can take that path, else null
+  hipStream_t aux = nullptr;
 };
 
 namespace {
@@ -105,8 +109,9 @@ struct Plan {
 };
 
 // Rows from which a group leaves the streaming GEMMs for the LDS-tiled ones
-// in a load-imbalanced batch.
+// in a load-imbalanced batch, and the smallest batch that does so.
 constexpr int kHotRows = 32;
+constexpr int kHybridMinTokens = 256;
 
 Plan make_plan(const moe_layer& L, int T) {
   const moe_layer_config_t& c = L.cfg;
@@ -145,7 +150,7 @@ Plan make_plan(const moe_layer& L, int T) {
   // where the hot experts' few tiles leave the extra launch mostly idle;
   // neutral on uniform routing.
   p.hybrid = !p.tiled && !p.large_dispatch && c.weight_dtype == MOE_BF16 &&
-             c.act_dtype == MOE_BF16 && T >= 256;
+             c.act_dtype == MOE_BF16 && T >= kHybridMinTokens;
   p.hot = p.hybrid ? kHotRows : 0;
   p.tg2 = 8;
   const int bm = 16 * p.tg;
@@ -256,11 +261,27 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, int device, moe_lay
   L->device = device;
   L->expert_bytes = packed_group_bytes(*cfg, cfg->inter);
   L->shared_bytes = cfg->shared_inter ? packed_group_bytes(*cfg, cfg->shared_inter) : 0;
+  if (cfg->weight_dtype == MOE_BF16 && cfg->act_dtype == MOE_BF16 &&
+      cfg->max_tokens >= kHybridMinTokens) {
+    DeviceGuard dg(device);
+    e = dg.err != hipSuccess ? dg.err : hipStreamCreateWithFlags(&L->aux, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      delete L;
+      return fail(MOE_ERR_DEVICE, "hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+    }
+  }
   *out = L;
   return ok();
 }
 
-void moe_layer_destroy(moe_layer_t layer) { delete layer; }
+void moe_layer_destroy(moe_layer_t layer) {
+  if (!layer) return;
+  if (layer->aux) {  // its pending work completes before its resources are released
+    DeviceGuard dg(layer->device);
+    (void)hipStreamDestroy(layer->aux);
+  }
+  delete layer;
+}
 
 size_t moe_layer_packed_bytes(moe_layer_t L) {
   if (!L) return 0;
@@ -435,15 +456,37 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   } else {
     uint16_t* hl = reinterpret_cast<uint16_t*>(ws + p.h_lo);
     uint16_t* h2 = reinterpret_cast<uint16_t*>(ws + p.h2);
+    // The hot experts' LDS-tiled gate/up and down -- few, long-running
+    // workgroups -- go to the handle's second stream, forked after the
+    // dispatch and joined before the combine, where they overlap the
+    // streaming GEMMs on the caller's stream (they write h2 and their own rows
+    // of Y only).  The events exist for this call only; without them (a failed
+    // creation) the same launches run in order on the caller's stream.
+    hipEvent_t fork = nullptr, join = nullptr;
+    hipStream_t s2 = stream;
+    if (e == hipSuccess && p.hybrid && L->aux &&
+        hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess) {
+      e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventRecord(fork, stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(L->aux, fork, 0);
+      if (e == hipSuccess) s2 = L->aux;
+    }
+    if (e == hipSuccess && p.hybrid) {
+      e = moe::launch_gateup_tiled(g2, static_cast<const uint16_t*>(x), row_tok, h2, nullptr,
+                                   p.hstride, s2);
+      if (e == hipSuccess) e = moe::launch_down_tiled(g2, h2, nullptr, p.hstride, y, s2);
+    }
     if (e == hipSuccess)
       e = moe::launch_gateup(g, int4, f32, x, row_tok, h, hl, p.hstride, stream);
-    if (e == hipSuccess && p.hybrid)
-      e = moe::launch_gateup_tiled(g2, static_cast<const uint16_t*>(x), row_tok, h2, nullptr,
-                                   p.hstride, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = moe::launch_down(g, int4, f32, h, hl, p.hstride, y, stream);
-    if (e == hipSuccess && p.hybrid)
-      e = moe::launch_down_tiled(g2, h2, nullptr, p.hstride, y, stream);
+    if (s2 != stream) {  // also after a failed launch: the caller's stream must not run ahead
+      hipError_t r = hipEventRecord(join, s2);
+      if (r == hipSuccess) r = hipStreamWaitEvent(stream, join, 0);
+      if (e == hipSuccess) e = r;
+    }
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
   }
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)

@@ -356,6 +356,32 @@ def test_verify_256_zipf():
     assert counts.max() > 150 and (counts > 0).sum() > 200   # skewed and wide
 
 
+@pytest.mark.parametrize("tokens", [128, 512])
+def test_batch_sizes_around_the_second_stream(tokens):
+    """Zipf-routed batches below and above 256 tokens, through a handle that
+    owns a second stream: at 128 tokens everything runs in order on the
+    caller's stream and equals, bit for bit, a handle without a second stream
+    (max_tokens 128); at 512 tokens the hot experts' LDS-tiled GEMMs run on
+    the second stream, overlapping the streaming GEMMs.  Both against the
+    oracle on sampled tokens."""
+    s = W["verify"].replace(name=f"verify_{tokens}_aux", tokens=tokens)
+    inp = moe_synth.make_layer(s, seed=0, device="cuda")
+    side = make_layer(s, max_tokens=1024)
+    side.pack_inputs(inp)
+    out, route = run_gpu(side, inp)
+    _say(s.name, "handle with a second stream")
+    if tokens < 256:
+        inorder = make_layer(s, max_tokens=tokens)
+        inorder.pack_inputs(inp)
+        ref, _ = run_gpu(inorder, inp)
+        assert torch.equal(out, ref)
+    else:
+        counts = route.expert_counts.cpu().numpy()
+        assert (counts >= 32).sum() >= 3, counts    # hot experts: LDS tiles on the second stream
+    res = compare(inp, out, route, sample=_spread(tokens, 24), strict=True)
+    _say("ok", res)
+
+
 def test_prefill_16384_sampled():
     _run(W["prefill"], sample=_spread(16384, 24))
 
