@@ -18,7 +18,8 @@ def test_more_than_one_gpu_is_refused():
 def test_counters_follow_the_kernel_sources(tmp_path, monkeypatch):
     import bench
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    srcs = bench.GEMM_SRC["verify"]
+    srcs = [bench._STREAM, bench._TILED]           # a stage of two kernels' sources
+    monkeypatch.setitem(bench.GEMM_SRC, "verify", srcs)
     good = ",".join(bench.src_digest(p) for p in srcs)
     f = tmp_path / "gate_up_verify_counters.txt"
     f.write_text(f"# comment: ignored\nsrc_sha: {good}\nfetch_bytes: 1000\nwrite_bytes: 24\n")
