@@ -91,6 +91,26 @@ def read_counters(workload: str):
         return None
 
 
+def device_info():
+    """Name, CU count and peak shader clock of cuda:0 as the HIP runtime reports
+    them, and the dense bf16 MFMA rate they imply (4096 flop per clock per CU)."""
+    import ctypes as C
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    hip = C.CDLL("libamdhip64.so.7")
+    hip.hipDeviceGetAttribute.argtypes = [C.POINTER(C.c_int), C.c_int, C.c_int]
+    # hipDeviceAttribute_t values (hip_runtime_api.h): ClockRate (kHz) 5, MultiprocessorCount 63
+    vals = {}
+    for name, attr in (("clock_khz", 5), ("cus", 63)):
+        v = C.c_int(0)
+        vals[name] = v.value if hip.hipDeviceGetAttribute(C.byref(v), attr, 0) == 0 else None
+    info = {"name": props.name, "arch": props.gcnArchName.split(":")[0], "cus": vals["cus"],
+            "sclk_peak_mhz": None if vals["clock_khz"] is None else vals["clock_khz"] / 1000}
+    if vals["cus"] and vals["clock_khz"]:
+        info["bf16_dense_tflops_at_peak_sclk"] = round(vals["cus"] * 4096 * vals["clock_khz"] * 1e3 / 1e12, 1)
+    return info
+
+
 def cpu_baseline(inp, shape, target_s: float):
     """The oracle as it stands, on the host cores, on the first S tokens of the
     same batch (S doubled until the run takes about target_s seconds)."""
@@ -273,6 +293,8 @@ def main():
                    **({"swiglu_limits": [shape.swiglu_limit, shape.swiglu_limit_shared]}
                       if shape.swiglu_limit or shape.swiglu_limit_shared else {})},
         "roofline": roof,
+        "device": {**device_info(),
+                   "peaks_used": "published: HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s"},
         "layer": {**layer_frac, "alg_bytes": int(b_alg), "alg_flops": int(f_alg),
                   "experts_touched": U,
                   "stage_ms": {n: round(v, 5) for n, v in zip(B.STAGES, stage_avg)}},

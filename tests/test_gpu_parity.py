@@ -386,6 +386,16 @@ def test_prefill_16384_sampled():
     _run(W["prefill"], sample=_spread(16384, 24))
 
 
+def test_max_tokens_sampled():
+    """The largest batch a handle accepts (2^18 tokens) at the full layer shape:
+    Y alone holds (P+T)*H ~ 2.4e9 elements, past 32-bit indexing.  The
+    dispatch of every pair is compared bit for bit, routing and outputs on
+    sampled tokens (the first, middle and last among them)."""
+    T = 1 << 18
+    s = W["prefill"].replace(name="max_tokens", tokens=T)
+    _run(s, sample=_spread(T, 16), cmp_kw={"strict": True})
+
+
 def test_int4_decode_32():
     _run(W["int4_decode"])
 
