@@ -13,7 +13,12 @@ Workloads (seeded synthetic inputs, shapes from the llm-atlas "Step-3.5-Flash"
 config fields): decode (32 tokens, default), verify (256 tokens, Zipf expert
 popularity), prefill (16384 tokens), int4_decode (32 tokens, INT4-g32 weights),
 mtp_decode (32 tokens through a last layer: SwiGLU limits 7 routed / 16 shared,
-activations drawn 8x wider so that the limits act), tiny (parity-sized).
+activations drawn 8x wider so that the limits act), page_router_decode (32
+tokens under the page's router configuration: sigmoid scores, a seeded
+per-expert router bias, weights x3), step3_decode / step3_prefill (Step-3's
+MoE shape: hidden 7168, 48 experts, top-3, width 5120, no renormalisation; 32
+and 4096 tokens), dense_decode / dense_prefill (the dense SwiGLU FFN of width
+11264 as one expert; 32 and 16384 tokens), tiny (parity-sized).
 """
 from __future__ import annotations
 
@@ -37,7 +42,12 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_layer_amd", "csrc")
 # prefill batch, weight-streaming GEMMs for the decode-sized ones
 _STREAM = os.path.join(CSRC, "moe_gemm_stream.hip")
 _TILED = os.path.join(CSRC, "moe_gemm_tiled.hip")
-GEMM_SRC = {"prefill": [_TILED]}
+GEMM_SRC = {"prefill": [_TILED], "step3_prefill": [_TILED], "dense_prefill": [_TILED]}
+# workloads whose roofline is the MFMA peak (the LDS-tiled regime); the rest are HBM-bound
+MFMA_BOUND = ("prefill", "step3_prefill", "dense_prefill")
+WORKLOAD_NAMES = ["tiny", "decode", "verify", "prefill", "int4_decode", "mtp_decode",
+                  "page_router_decode", "step3_decode", "step3_prefill", "dense_decode",
+                  "dense_prefill"]
 GEMM_SRC_DEFAULT = [_STREAM]
 
 
@@ -51,7 +61,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "verify", "prefill", "int4_decode", "mtp_decode"])
+                    choices=WORKLOAD_NAMES)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle on the host (e.g. under a profiler)")
@@ -151,11 +161,13 @@ def cpu_baseline(inp, shape, target_s: float):
     T = x64.shape[0]
     s, elapsed = 1, 0.0
     while True:
-        idx, *_ = oracle.route(x64[:s], wr, bias, shape.top_k)
+        idx, *_ = oracle.route(x64[:s], wr, bias, shape.top_k, shape.score, shape.renormalize,
+                               shape.routed_scale, shape.bias_mode)
         for e in np.unique(idx):
             fetch(int(e))
         t0 = time.perf_counter()
-        oracle.forward(x64[:s], wr, bias, experts, shared, shape.top_k,
+        oracle.forward(x64[:s], wr, bias, experts, shared, shape.top_k, shape.score,
+                       shape.renormalize, shape.routed_scale, shape.bias_mode,
                        swiglu_limit=shape.swiglu_limit, swiglu_limit_shared=shape.swiglu_limit_shared)
         elapsed = time.perf_counter() - t0
         if elapsed >= target_s or s >= T:
@@ -233,7 +245,7 @@ def main():
     t_layer = ms / 1e3
     gu_ms = stage_avg[2]
     Us = U
-    if args.workload == "prefill":
+    if args.workload in MFMA_BOUND:
         gu_flops = 4.0 * H * (P * I + T * Is)
         achieved = gu_flops / (gu_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16 / 1e12,
@@ -257,7 +269,7 @@ def main():
                 "traffic": read_counters(args.workload)}
         layer_frac = {"hbm_frac": round(b_alg / t_layer / PEAK_HBM, 4)}
     roof["kernel"] = "gate_up (grouped gate/up GEMM + SiLU*up)"
-    if args.workload != "prefill" and Us != U:
+    if args.workload not in MFMA_BOUND and Us != U:
         roof["kernel"] += f" streaming launch: {Us} of {U} routed experts + shared"
 
     cpu = None
@@ -270,7 +282,13 @@ def main():
                "verify": "Step-3.5-Flash MoE layer, MTP verify batch (64 streams x 4), Zipf experts",
                "prefill": "Step-3.5-Flash MoE layer, prefill chunk",
                "int4_decode": "Step-3.5-Flash MoE layer, decode batch, INT4-g32 weights",
-               "mtp_decode": "Step-3.5-Flash last MoE layer (SwiGLU limits 7 / 16), decode batch"}
+               "mtp_decode": "Step-3.5-Flash last MoE layer (SwiGLU limits 7 / 16), decode batch",
+               "page_router_decode": "Step-3.5-Flash MoE layer under the page's router config "
+                                     "(sigmoid, router bias, x3), decode batch",
+               "step3_decode": "Step-3 MoE layer shape, decode batch",
+               "step3_prefill": "Step-3 MoE layer shape, 4096-token chunk",
+               "dense_decode": "dense SwiGLU FFN (width 11264) as one expert, decode batch",
+               "dense_prefill": "dense SwiGLU FFN (width 11264) as one expert, prefill chunk"}
     line = {
         "metric": METRIC,
         "value": round(T / t_layer, 1),
@@ -283,13 +301,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if not int4 else "bf16 x int4-g32",
-        "data": (f"synthetic (seeded N(0,{shape.x_scale:g}^2) activations, N(0,1/fan_in) weights)"
-                 if shape.x_scale != 1.0 else
-                 "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)"),
+        "data": (f"synthetic (seeded N(0,{shape.x_scale:g}^2) activations, N(0,1/fan_in) weights"
+                 + {"zipf": ", Zipf-calibrated router bias", "bias": ", N(0,0.1^2) router bias"}
+                 .get(shape.routing, "") + ")"),
         "config": {"workload": f"{args.workload}: {wl_desc[args.workload]}", "tokens": T,
                    "hidden": H, "experts": E, "top_k": k, "expert_inter": I,
                    "shared_inter": Is, "weights": shape.weight_dtype,
                    "routing": shape.routing, "parallelism": "single GPU",
+                   "renormalize": shape.renormalize,
+                   **({"score": shape.score, "routed_scale": shape.routed_scale,
+                       "bias_mode": shape.bias_mode}
+                      if shape.score != "softmax" or shape.routed_scale != 1.0 else {}),
                    **({"swiglu_limits": [shape.swiglu_limit, shape.swiglu_limit_shared]}
                       if shape.swiglu_limit or shape.swiglu_limit_shared else {})},
         "roofline": roof,

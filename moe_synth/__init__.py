@@ -44,12 +44,16 @@ class LayerShape:
     shared_inter: int
     act_dtype: str = "bf16"        # "bf16" | "f32"
     weight_dtype: str = "bf16"     # "bf16" | "int4_g32"
-    routing: str = "uniform"       # "uniform" (no bias) | "zipf" (per-expert logit bias)
+    routing: str = "uniform"       # "uniform" (no bias) | "zipf" (Zipf-calibrated bias) |
+                                   # "bias" (seeded N(0, 0.1^2) per-expert bias)
     renormalize: bool = True
     index: int = 0                 # workload index, part of every seed
     x_scale: float = 1.0           # activations drawn from N(0, x_scale^2)
     swiglu_limit: float = 0.0      # routed experts' SwiGLU limit (0 = none)
     swiglu_limit_shared: float = 0.0  # shared expert's SwiGLU limit (0 = none)
+    score: str = "softmax"         # router scores: "softmax" | "sigmoid"
+    routed_scale: float = 1.0      # factor on the routed weights
+    bias_mode: str = "logit"       # router bias in the logits ("logit") or the selection only
 
     @property
     def pairs(self) -> int:
@@ -63,6 +67,11 @@ class LayerShape:
 
 
 STEP35 = dict(hidden=4096, experts=288, top_k=8, inter=1280, shared_inter=1280)
+# Step-3's MoE layer (llm-atlas "Step-3.5-Flash", table comparing it with
+# Step-3): hidden 7168, 48 experts, top-3, width 5120, no renormalisation
+STEP3 = dict(hidden=7168, experts=48, top_k=3, inter=5120, shared_inter=5120, renormalize=False)
+# the dense SwiGLU FFN of the first layers (intermediate_size 11264) as one expert
+DENSE = dict(hidden=4096, experts=1, top_k=1, inter=11264, shared_inter=0)
 
 # The workloads.  Index 0 is the tiny case the oracle finishes in
 # milliseconds; 1 is single-stream-batch decode; 2 is a multi-token-prediction
@@ -73,7 +82,13 @@ STEP35 = dict(hidden=4096, experts=288, top_k=8, inter=1280, shared_inter=1280)
 # swiglu_limits_shared), with activations drawn 8x wider so that the clamps
 # act: the projections then have a standard deviation near 8, and about a
 # third of the routed up values and a twentieth of the shared ones lie beyond
-# their limit.
+# their limit.  6 is decode under the page's router configuration (sigmoid
+# scores, a per-expert router bias -- drawn N(0, 0.1^2) here, the pages give
+# no values -- and routed weights scaled by 3; llm-atlas config fields
+# moe_router_activation, use_moe_router_bias, moe_router_scaling_factor);
+# 7 and 8 are Step-3's MoE shape at a decode batch and a 4096-token chunk
+# (256 rows per expert); 9 and 10 are the dense FFN as one expert at a
+# decode batch and a 16384-token chunk.
 WORKLOADS = {
     "tiny": LayerShape("tiny", 64, 256, 16, 2, 64, 64, act_dtype="f32", index=0),
     "decode": LayerShape("decode", 32, **STEP35, index=1),
@@ -82,10 +97,16 @@ WORKLOADS = {
     "int4_decode": LayerShape("int4_decode", 32, **STEP35, weight_dtype="int4_g32", index=4),
     "mtp_decode": LayerShape("mtp_decode", 32, **STEP35, x_scale=8.0, swiglu_limit=7.0,
                              swiglu_limit_shared=16.0, index=5),
+    "page_router_decode": LayerShape("page_router_decode", 32, **STEP35, routing="bias",
+                                     score="sigmoid", routed_scale=3.0, index=6),
+    "step3_decode": LayerShape("step3_decode", 32, **STEP3, index=7),
+    "step3_prefill": LayerShape("step3_prefill", 4096, **STEP3, index=8),
+    "dense_decode": LayerShape("dense_decode", 32, **DENSE, index=9),
+    "dense_prefill": LayerShape("dense_prefill", 16384, **DENSE, index=10),
 }
 
 # tensor ids (part of the seed)
-T_X, T_ROUTER, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN = range(8)
+T_X, T_ROUTER, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN, T_BIAS = range(9)
 
 
 def seed_for(seed: int, workload: int, tensor: int, expert: int = 0) -> int:
@@ -181,6 +202,8 @@ def make_layer(shape: LayerShape, seed: int = 0, device="cpu",
     bias = None
     if shape.routing == "zipf":
         bias = torch.from_numpy(zipf_bias(E)).to(dev)
+    elif shape.routing == "bias":
+        bias = _normal((E,), 0.1, dev, seed_for(seed, wl, T_BIAS), torch.float32)
     out = LayerInputs(shape, x, router_w, bias)
 
     def stacked(tensor_id, n, k, fan_in):

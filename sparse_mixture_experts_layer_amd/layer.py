@@ -90,7 +90,10 @@ class MoELayer:
                    act_dtype=torch.float32 if shape.act_dtype == "f32" else torch.bfloat16,
                    weight_dtype=shape.weight_dtype, device=device,
                    **{"swiglu_limit": getattr(shape, "swiglu_limit", 0.0),
-                      "swiglu_limit_shared": getattr(shape, "swiglu_limit_shared", 0.0), **kw})
+                      "swiglu_limit_shared": getattr(shape, "swiglu_limit_shared", 0.0),
+                      "score": getattr(shape, "score", "softmax"),
+                      "routed_scale": getattr(shape, "routed_scale", 1.0),
+                      "bias_mode": getattr(shape, "bias_mode", "logit"), **kw})
 
     def close(self) -> None:
         if getattr(self, "_h", None):

@@ -72,11 +72,16 @@ def run_gpu(layer, inp, tokens=None, seed_ws=None):
     return out, route
 
 
-def compare(inp, out, route, sample=None, score="softmax", renormalize=True, routed_scale=1.0,
-            bias_mode="logit", k=None, tokens=None, strict=True):
-    """Checks one GPU forward against the oracle; returns a dict of figures."""
+def compare(inp, out, route, sample=None, score=None, renormalize=None, routed_scale=None,
+            bias_mode=None, k=None, tokens=None, strict=True):
+    """Checks one GPU forward against the oracle; returns a dict of figures.
+    The router settings default to the shape's."""
     shape = inp.shape
     k = k or shape.top_k
+    score = shape.score if score is None else score
+    renormalize = shape.renormalize if renormalize is None else renormalize
+    routed_scale = shape.routed_scale if routed_scale is None else routed_scale
+    bias_mode = shape.bias_mode if bias_mode is None else bias_mode
     T = out.shape[0]
     x64 = moe_synth.host_f64(inp.x[:T])
     wr = moe_synth.host_f64(inp.router_w)

@@ -449,6 +449,17 @@ def test_dense_ffn_as_one_expert(tokens):
     _run(s, sample=_spread(tokens, 8) if tokens > 64 else None)
 
 
+@pytest.mark.parametrize("name,sampled", [("page_router_decode", 0), ("step3_decode", 0),
+                                          ("step3_prefill", 12), ("dense_decode", 0),
+                                          ("dense_prefill", 12)])
+def test_next_row_workloads(name, sampled):
+    """The benchmarked workloads of the widened rows, as bench.py times them:
+    the page's router configuration, Step-3's shape, the dense FFN as one
+    expert (every token, or sampled ones in the large batches)."""
+    s = W[name]
+    _run(s, sample=_spread(s.tokens, sampled) if sampled else None)
+
+
 # ----------------------------------------------------------------- SwiGLU limits
 
 LIMITS = dict(swiglu_limit=0.5, swiglu_limit_shared=0.75)   # act on N(0, 1) projections
