@@ -103,6 +103,8 @@ struct Plan {
   // hybrid: streaming GEMMs for most groups, LDS-tiled ones (tg2, list 2) for
   // the groups with `hot` rows or more
   int hybrid, hot, tg2, max_tiles2;
+  // the LDS-tiled down GEMM's K split (Y then holds ksplit partial-sum planes)
+  int ksplit;
   size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, tiles2, ntiles2,
       done, blk_hist, h, h_lo, h2, y, total;
   int large_dispatch;
@@ -138,6 +140,21 @@ Plan make_plan(const moe_layer& L, int T) {
   // 142-178 rows), but a tile that is mostly padding below that (96-114
   // rows: 128-row tiles 10% ahead)
   if (p.tiled) p.tg = rows_per_expert >= 128.0 ? 16 : 8;
+  // A tiled batch with few tiles (one expert or a handful, e.g. a dense FFN
+  // as one expert at a decode batch) would run its down GEMM -- K = the
+  // expert width, up to thousands -- on a few dozen workgroups: K is split
+  // into up to 16 parts, each writing its own partial-sum plane of Y, until
+  // the launch has ~512 workgroups (the bound below counts every tile the
+  // dispatch could write, so real batches use fewer).
+  p.ksplit = 1;
+  if (p.tiled) {
+    const int nz0 = c.num_experts < p.P ? c.num_experts : p.P;
+    const long bound = ((long)nz0 + p.P / (16 * p.tg) + (p.has_shared ? T / (16 * p.tg) + 1 : 0) + 1) *
+                       ((c.hidden + 255) / 256);
+    while (bound * p.ksplit < 512 && p.ksplit < 16 && (c.inter / 32) % (2 * p.ksplit) == 0 &&
+           (c.shared_inter / 32) % (2 * p.ksplit) == 0)
+      p.ksplit *= 2;
+  }
   // one workgroup dispatches small batches; larger ones use per-block counts
   p.large_dispatch = T > 1024;
   // Streaming batches whose routing is uneven (a Zipf-popular expert can
@@ -194,7 +211,7 @@ Plan make_plan(const moe_layer& L, int T) {
                           : (size_t)T * p.hstride * 2);
   // the hybrid's LDS-tiled groups (routed only): packed h of their own
   p.h2 = take(p.hybrid ? h_rows_tiled * p.hstride * 2 : 0);
-  p.y = take((size_t)rows * c.hidden * 4);
+  p.y = take((size_t)p.ksplit * rows * c.hidden * 4);
   p.total = o;
   return p;
 }
@@ -439,6 +456,8 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g.shared_tiles = p.has_shared ? (T + 16 * p.tg - 1) / (16 * p.tg) : 0;
   g.limit = c.swiglu_limit;
   g.limit_shared = c.swiglu_limit_shared;
+  g.ksplit = p.ksplit;
+  g.y_plane = (size_t)(p.P + (p.has_shared ? T : 0)) * H;
   moe::GemmGeom g2 = g;  // the hybrid's LDS-tiled groups
   g2.tiles = reinterpret_cast<int32_t*>(ws + p.tiles2);
   g2.ntiles = reinterpret_cast<int32_t*>(ws + p.ntiles2);
@@ -490,7 +509,8 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   }
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
-    e = moe::launch_combine(f32, y, H, inv, wts, k, p.P, p.has_shared, out, T, stream);
+    e = moe::launch_combine(f32, y, H, inv, wts, k, p.P, p.has_shared, out, T, p.ksplit,
+                            g.y_plane, stream);
   if (e == hipSuccess) e = mark(5);
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   if (route) {

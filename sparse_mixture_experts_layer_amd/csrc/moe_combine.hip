@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int k, int P,
                                                       int has_shared, void* __restrict__ out,
-                                                      int T) {
+                                                      int T, int planes, size_t plane) {
   const int t = blockIdx.x;
   const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
   if (t >= T || col >= H) return;
@@ -38,11 +38,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   // shared row (or, without a shared expert, any valid row, then zeroed)
   const size_t srow = has_shared ? (size_t)(P + t) : (size_t)rows[0];
-  const f32x4 sh = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + srow * H + col));
+  f32x4 sh = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + srow * H + col));
   f32x4 v[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j)
     v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)rows[j] * H + col));
+  // rows split into partial-sum planes (a down GEMM with a split K): each row's
+  // planes added in order
+  for (int q = 1; q < planes; ++q) {
+    const float* yq = y + q * plane;
+    sh += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yq + srow * H + col));
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      v[j] += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yq + (size_t)rows[j] * H + col));
+  }
   // fixed order: shared, then j = 0 .. k-1
   f32x4 acc = has_shared ? sh : zero;
 #pragma unroll
@@ -70,7 +79,8 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
                                                            const int32_t* __restrict__ inv,
                                                            const float* __restrict__ w, int k,
                                                            int P, int has_shared,
-                                                           void* __restrict__ out, int T) {
+                                                           void* __restrict__ out, int T,
+                                                           int planes, size_t plane) {
   const int t = blockIdx.x;
   if (t >= T) return;
   __shared__ int rows[kMaxTopK];
@@ -96,6 +106,13 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
       if (has_shared && col[i] < H)
         acc[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)(P + t) * H + col[i]));
     }
+    if (has_shared)  // partial-sum planes of a split-K down GEMM
+      for (int q = 1; q < planes; ++q)
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i)
+          if (col[i] < H)
+            acc[i] += __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(y + q * plane + (size_t)(P + t) * H + col[i]));
     for (int j = 0; j < k; ++j) {
       const float* yr = y + (size_t)rows[j] * H;
       const float wj = ws[j];
@@ -103,6 +120,11 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
 #pragma unroll
       for (int i = 0; i < kChunks; ++i)
         v[i] = col[i] < H ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yr + col[i])) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 1; q < planes; ++q)  // partial-sum planes of a split-K down GEMM
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i)
+          if (col[i] < H)
+            v[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yr + q * plane + col[i]));
 #pragma unroll
       for (int i = 0; i < kChunks; ++i)
 #pragma unroll
@@ -126,22 +148,23 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
-                          int k, int P, int has_shared, void* out, int T, hipStream_t s) {
-  if (k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
+                          int k, int P, int has_shared, void* out, int T, int planes,
+                          size_t plane, hipStream_t s) {
+  if (k < 1 || k > kMaxTopK || planes < 1) return hipErrorInvalidValue;
   if (T >= 512) {  // bandwidth-bound: whole rows per workgroup
     dim3 grid(T), block(256);
     if (out_f32)
       hipLaunchKernelGGL((combine_rows_kernel<true>), grid, block, 0, s, y, H, inv, w, k, P,
-                         has_shared, out, T);
+                         has_shared, out, T, planes, plane);
     else
       hipLaunchKernelGGL((combine_rows_kernel<false>), grid, block, 0, s, y, H, inv, w, k, P,
-                         has_shared, out, T);
+                         has_shared, out, T, planes, plane);
     return hipGetLastError();
   }
   dim3 grid(T, (H / 4 + 255) / 256), block(256);
 #define MOE_CB(F32, KM)                                                                          \
   hipLaunchKernelGGL((combine_kernel<F32, KM>), grid, block, 0, s, y, H, inv, w, k, P, has_shared, \
-                     out, T)
+                     out, T, planes, plane)
 #define MOE_CB_K(F32)                   \
   if (k <= 2) MOE_CB(F32, 2);           \
   else if (k <= 4) MOE_CB(F32, 4);      \

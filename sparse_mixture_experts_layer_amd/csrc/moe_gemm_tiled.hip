@@ -101,6 +101,13 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   //     each XCD keeps a slice of them and the h tiles in its L2.
   const int total = *g.ntiles * nblk;
   int w = (int)blockIdx.x;
+  // down with a split K: the work list repeats once per part, part slowest
+  int split = 0;
+  if (MODE == 1 && g.ksplit > 1) {
+    split = w / total;
+    if (split >= g.ksplit) return;
+    w -= split * total;
+  }
   if (MODE == 0) {
     const int chunk = (total + kXcds - 1) / kXcds;
     const int slot = blockIdx.x / kXcds;
@@ -133,7 +140,9 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int K = MODE == 0 ? H : width;
-  const int nk = K / 32;
+  // k-steps of this workgroup: all of K, or part `split` of ksplit (down)
+  const int nk = MODE == 1 ? K / 32 / g.ksplit : K / 32;
+  const int kbeg = split * nk;
   // weight blocks of 64 rows (gate/up: 32 features x {gate, up}; down: 64 outputs)
   const int nblocks = MODE == 0 ? width / 32 : H / 64;
 
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         // packed h: rows past nrows read the padding behind the group (inside
         // the buffer, whatever it holds); their C rows are never stored
         const int b = (pass == 0 ? hb0 : mt * (TM / 16)) + 2 * wave + f;
-        a_off[f] = (size_t)b * hkb * (kFragBytes / 2) + lane * 8;
+        a_off[f] = ((size_t)b * hkb + kbeg) * (kFragBytes / 2) + lane * 8;
       }
     }
   };
@@ -185,8 +194,9 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   const int bblk = nb * 4 + kBL * wave / 4;
   const uint8_t* bsrc = g.packed + (size_t)group * g.expert_bytes +
                         (MODE == 0 ? 0 : (size_t)2 * width * H * 2) +
-                        (size_t)(bblk < nblocks ? bblk : 0) * nk * 4 * kFragBytes +
-                        (kBL * wave % 4) * kFragBytes + lane * 16;
+                        (size_t)(bblk < nblocks ? bblk : 0) * (K / 32) * 4 * kFragBytes +
+                        (size_t)kbeg * 4 * kFragBytes + (kBL * wave % 4) * kFragBytes +
+                        lane * 16;
 
   const uint16_t* a_base = a_src;
   // elements from one k-step to the next: 32 along an x row, one fragment in packed h
@@ -357,8 +367,8 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         const int blk = blk0 + (ch >> 4);
         if (r < nrows && blk < nblocks)  // read once, by combine: nontemporal
           __builtin_nontemporal_store(
-              val, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)(row0 + r) * H +
-                                            blk * 64 + (ch & 15) * 4));
+              val, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + split * g.y_plane +
+                                            (size_t)(row0 + r) * H + blk * 64 + (ch & 15) * 4));
       }
     }
     return;
@@ -415,7 +425,8 @@ hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_
   const int tm = 16 * g.tg;
   if (tm != 128 && tm != 256) return hipErrorInvalidValue;
   const int nblk = (g.H + kTN - 1) / kTN;
-  const size_t items = (size_t)g.max_tiles * nblk;
+  if (g.ksplit < 1 || (g.I / 32) % g.ksplit || (g.Is / 32) % g.ksplit) return hipErrorInvalidValue;
+  const size_t items = (size_t)g.max_tiles * nblk * g.ksplit;
   dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(2 * tm);
   if (tm == 256)
     hipLaunchKernelGGL((tiled_kernel<1, 256>), grid, block, 0, s, g, h, nullptr, y, hstride,

@@ -61,6 +61,11 @@ struct GemmGeom {
   int tg;                     // token groups of 16 per tile (tile rows = 16 * tg)
   int shared_tiles;           // tiles of the shared group at the end of this list (0: none)
   float limit, limit_shared;  // SwiGLU limits of the routed / shared experts (0 = none)
+  // LDS-tiled down GEMM only: K split into ksplit equal parts (ksplit divides
+  // every group's width/32), part s writing its partial sums to Y plane s, y_plane
+  // floats after plane s-1 (the combine adds the planes in order)
+  int ksplit;
+  size_t y_plane;
 };
 
 // h[row][f] = silu(x W_gate^T) * (x W_up^T) for every permuted row; h is fp32
@@ -91,8 +96,11 @@ hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_
                              int hstride, float* y, hipStream_t s);
 
 // ---- combine: out[t] = Y[shared row of t] + sum_j w[t,j] Y[inv[t,j]] -------
+// Y may come in `planes` partial-sum planes, `plane` floats apart: each row is
+// then the sum of its planes, added in plane order.
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
-                          int k, int P, int has_shared, void* out, int T, hipStream_t s);
+                          int k, int P, int has_shared, void* out, int T, int planes,
+                          size_t plane, hipStream_t s);
 
 // ---- weight packing ----------------------------------------------------------
 // bf16 [N][K] of S sources (1 or 2) -> blocks of F*S fragments per 32-k step.
