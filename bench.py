@@ -38,11 +38,12 @@ PEAK_BF16 = 2.5e15         # flop/s, MI355X dense bf16 MFMA (published)
 HOT_ROWS = 32              # the library's threshold for a hot expert's LDS tiles
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_layer_amd", "csrc")
-# sources of the gate/up stage's kernels per workload: LDS-tiled GEMMs for the
-# prefill batch, weight-streaming GEMMs for the decode-sized ones
+# sources of the gate/up stage's kernels per workload: LDS-tiled GEMMs from 16
+# rows per expert, weight-streaming GEMMs below
 _STREAM = os.path.join(CSRC, "moe_gemm_stream.hip")
 _TILED = os.path.join(CSRC, "moe_gemm_tiled.hip")
-GEMM_SRC = {"prefill": [_TILED], "step3_prefill": [_TILED], "dense_prefill": [_TILED]}
+GEMM_SRC = {"prefill": [_TILED], "step3_prefill": [_TILED], "dense_prefill": [_TILED],
+            "dense_decode": [_TILED]}   # one expert with 32 rows: LDS-tiled as well
 # workloads whose roofline is the MFMA peak (the LDS-tiled regime); the rest are HBM-bound
 MFMA_BOUND = ("prefill", "step3_prefill", "dense_prefill")
 WORKLOAD_NAMES = ["tiny", "decode", "verify", "prefill", "int4_decode", "mtp_decode",

@@ -118,12 +118,27 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   const int v0 = g.tiles[w / nblk];
   const int group = tile_group(v0);
   int nb, mt;
-  if (MODE == 0 || TM == 256) {  // m-tiles fastest inside the group
+  if (MODE == 0 || TM == 256) {  // m-tiles fastest inside the group, in blocks of kMB
     const int first = w / nblk - tile_m(v0);
     const int ntg = (g.counts[group] + TM - 1) / TM;
     const int local = w - first * nblk;
-    nb = local / ntg;
-    mt = local % ntg;
+    // A group with many m-tiles (the shared expert, or a dense FFN as one
+    // expert) walks them in blocks of kMB, all weight blocks per m block, so
+    // that the workgroups running together cover a few m-tiles x a few weight
+    // blocks rather than many m-tiles of one weight block (each k-step then
+    // needs ~12 distinct operand slices instead of ~33 among 32 tiles);
+    // groups of up to kMB m-tiles keep plain m-fastest order.
+    constexpr int kMB = 8;
+    const int full = ntg / kMB * kMB;
+    if (local < full * nblk) {
+      const int r = local % (kMB * nblk);
+      nb = r / kMB;
+      mt = local / (kMB * nblk) * kMB + r % kMB;
+    } else {
+      const int rem = ntg - full, r = local - full * nblk;
+      nb = r / rem;
+      mt = full + r % rem;
+    }
   } else {                       // weight blocks fastest (measured better here)
     nb = w % nblk;
     mt = tile_m(v0);
