@@ -104,7 +104,9 @@ struct Plan {
   // the groups with `hot` rows or more
   int hybrid, hot, tg2, max_tiles2;
   // the LDS-tiled down GEMM's K split (Y then holds ksplit partial-sum planes)
-  int ksplit;
+  // and the gate/up's (partial gate/up planes in gu_part, reduced into h)
+  int ksplit, ksplit_gu;
+  size_t gu_part;
   size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, tiles2, ntiles2,
       done, blk_hist, h, h_lo, h2, y, total;
   int large_dispatch;
@@ -146,14 +148,23 @@ Plan make_plan(const moe_layer& L, int T) {
   // into up to 16 parts, each writing its own partial-sum plane of Y, until
   // the launch has ~512 workgroups (the bound below counts every tile the
   // dispatch could write, so real batches use fewer).
+  // The gate/up GEMM of such a batch splits K (H) the same way, up to 8
+  // parts of an even number of k-steps; its parts write fp32 partial sums of
+  // gate and up, and a reduction applies the SwiGLU.
   p.ksplit = 1;
+  p.ksplit_gu = 1;
   if (p.tiled) {
     const int nz0 = c.num_experts < p.P ? c.num_experts : p.P;
-    const long bound = ((long)nz0 + p.P / (16 * p.tg) + (p.has_shared ? T / (16 * p.tg) + 1 : 0) + 1) *
-                       ((c.hidden + 255) / 256);
+    const long tiles = (long)nz0 + p.P / (16 * p.tg) + (p.has_shared ? T / (16 * p.tg) + 1 : 0) + 1;
+    const long bound = tiles * ((c.hidden + 255) / 256);
     while (bound * p.ksplit < 512 && p.ksplit < 16 && (c.inter / 32) % (2 * p.ksplit) == 0 &&
            (c.shared_inter / 32) % (2 * p.ksplit) == 0)
       p.ksplit *= 2;
+    const int wmax = c.inter > c.shared_inter ? c.inter : c.shared_inter;
+    const long bound_gu = tiles * ((2 * wmax + 255) / 256);
+    while (bound_gu * p.ksplit_gu < 512 && p.ksplit_gu < 8 &&
+           (c.hidden / 32) % (4 * p.ksplit_gu) == 0)
+      p.ksplit_gu *= 2;
   }
   // one workgroup dispatches small batches; larger ones use per-block counts
   p.large_dispatch = T > 1024;
@@ -212,6 +223,7 @@ Plan make_plan(const moe_layer& L, int T) {
   // the hybrid's LDS-tiled groups (routed only): packed h of their own
   p.h2 = take(p.hybrid ? h_rows_tiled * p.hstride * 2 : 0);
   p.y = take((size_t)p.ksplit * rows * c.hidden * 4);
+  p.gu_part = take(p.ksplit_gu > 1 ? (size_t)p.ksplit_gu * rows * 2 * p.hstride * 4 : 0);
   p.total = o;
   return p;
 }
@@ -458,6 +470,9 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g.limit_shared = c.swiglu_limit_shared;
   g.ksplit = p.ksplit;
   g.y_plane = (size_t)(p.P + (p.has_shared ? T : 0)) * H;
+  g.ksplit_gu = p.ksplit_gu;
+  g.gu_part = p.ksplit_gu > 1 ? reinterpret_cast<float*>(ws + p.gu_part) : nullptr;
+  g.gu_plane = (size_t)(p.P + (p.has_shared ? T : 0)) * 2 * p.hstride;
   moe::GemmGeom g2 = g;  // the hybrid's LDS-tiled groups
   g2.tiles = reinterpret_cast<int32_t*>(ws + p.tiles2);
   g2.ntiles = reinterpret_cast<int32_t*>(ws + p.ntiles2);
@@ -470,6 +485,8 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     if (e == hipSuccess)
       e = moe::launch_gateup_tiled(g, static_cast<const uint16_t*>(x), row_tok, hb, hl,
                                    p.hstride, stream);
+    if (e == hipSuccess && p.ksplit_gu > 1)
+      e = moe::launch_gateup_reduce(g, p.P + (p.has_shared ? T : 0), hb, hl, p.hstride, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = moe::launch_down_tiled(g, hb, hl, p.hstride, y, stream);
   } else {

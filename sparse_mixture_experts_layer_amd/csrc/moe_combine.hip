@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)rows[j] * H + col));
   // rows split into partial-sum planes (a down GEMM with a split K): each row's
   // planes added in order
-  for (int q = 1; q < planes; ++q) {
+#pragma unroll 4
+  for (int q = 1; q < planes; ++q) {  // four planes' loads in flight together
     const float* yq = y + q * plane;
     sh += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yq + srow * H + col));
 #pragma unroll
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
 #pragma unroll
       for (int i = 0; i < kChunks; ++i)
         v[i] = col[i] < H ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yr + col[i])) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
       for (int q = 1; q < planes; ++q)  // partial-sum planes of a split-K down GEMM
 #pragma unroll
         for (int i = 0; i < kChunks; ++i)

@@ -101,18 +101,26 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   //     each XCD keeps a slice of them and the h tiles in its L2.
   const int total = *g.ntiles * nblk;
   int w = (int)blockIdx.x;
-  // down with a split K: the work list repeats once per part, part slowest
+  // a split K: the work list repeats once per part, part slowest (gate/up:
+  // per part a grid slice of a multiple of 8 workgroups, dealt as below)
+  const int nsplit = max(1, MODE == 1 ? g.ksplit : g.ksplit_gu);
   int split = 0;
-  if (MODE == 1 && g.ksplit > 1) {
+  if (MODE == 1 && nsplit > 1) {
     split = w / total;
-    if (split >= g.ksplit) return;
+    if (split >= nsplit) return;
     w -= split * total;
   }
   if (MODE == 0) {
+    int bid = (int)blockIdx.x;
+    if (nsplit > 1) {
+      const int per = (int)gridDim.x / nsplit;
+      split = bid / per;
+      bid -= split * per;
+    }
     const int chunk = (total + kXcds - 1) / kXcds;
-    const int slot = blockIdx.x / kXcds;
+    const int slot = bid / kXcds;
     if (slot >= chunk) return;
-    w = (blockIdx.x % kXcds) * chunk + slot;
+    w = (bid % kXcds) * chunk + slot;
   }
   if (w >= total) return;
   const int v0 = g.tiles[w / nblk];
@@ -155,8 +163,8 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int K = MODE == 0 ? H : width;
-  // k-steps of this workgroup: all of K, or part `split` of ksplit (down)
-  const int nk = MODE == 1 ? K / 32 / g.ksplit : K / 32;
+  // k-steps of this workgroup: all of K, or part `split` of nsplit
+  const int nk = K / 32 / nsplit;
   const int kbeg = split * nk;
   // weight blocks of 64 rows (gate/up: 32 features x {gate, up}; down: 64 outputs)
   const int nblocks = MODE == 0 ? width / 32 : H / 64;
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         int tok = row_tok[row0 + r];
         tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
         const int q = (lane & 7) ^ (lane >> 3);
-        a_off[u] = (size_t)tok * H + q * 8;
+        a_off[u] = (size_t)tok * H + (size_t)kbeg * 32 + q * 8;
       }
       return;
     }
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         if (r >= nrows) r = 0;  // any valid row: its C row is never stored
         int tok = row_tok[row0 + r];
         tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
-        a_off[f] = (size_t)tok * H + (lane >> 4) * 8;
+        a_off[f] = (size_t)tok * H + (size_t)kbeg * 32 + (lane >> 4) * 8;
       } else {
         // packed h: rows past nrows read the padding behind the group (inside
         // the buffer, whatever it holds); their C rows are never stored
@@ -388,6 +396,29 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     }
     return;
   }
+  if (MODE == 0 && nsplit > 1) {  // partial sums of part `split`: gate and up rows of fp32
+    float* gp = g.gu_part + split * g.gu_plane;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + m * 16 + (lane >> 4) * 4 + i;
+        if (r >= nrows) continue;
+        float* pr = gp + (size_t)(row0 + r) * 2 * hstride;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const int blk = nb * 4 + wn * 2 + jb;
+          if (blk >= nblocks) continue;
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const int feat = 32 * blk + 16 * f + (lane & 15);
+            pr[feat] = acc[m][jb * 4 + f][i];
+            pr[hstride + feat] = acc[m][jb * 4 + 2 + f][i];
+          }
+        }
+      }
+    return;
+  }
   // packed h: row rr of row-block b, feature 32*blk + 16*f + c sits in
   // fragment (b, blk) at lane rr + 16 * (2f + c/8), element c%8
 #pragma unroll
@@ -416,7 +447,70 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     }
 }
 
+// One thread per permuted row and 8 features: gate and up summed over the
+// K parts in order, SwiGLU, and the 8 bf16 results stored as one 16-byte
+// fragment lane of packed h (row r of group e at packed row
+// 16 * (ceil(offsets[e] / 16) + e) + (r - offsets[e]); the shared group's
+// remainder plane by its row).
+__global__ __launch_bounds__(256) void gateup_reduce_kernel(GemmGeom g, int rows,
+                                                            uint16_t* __restrict__ h,
+                                                            uint16_t* __restrict__ h_lo,
+                                                            int hstride) {
+  const int per_row = hstride / 8;
+  const int idx = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int row = idx / per_row, f8 = (idx % per_row) * 8;
+  if (row >= rows) return;
+  // the group holding this row: the last e with offsets[e] <= row (groups
+  // 0..E, offsets ascending; empty groups share an offset with the next)
+  int lo = 0, hi = g.E;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (g.offsets[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const int grp = lo;
+  const bool shared = grp == g.E;
+  const int width = shared ? g.Is : g.I;
+  if (f8 >= width) return;
+  const float lim = shared ? g.limit_shared : g.limit;
+  f32x4 gs[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, us[2] = {gs[0], gs[1]};
+  for (int sp = 0; sp < g.ksplit_gu; ++sp) {
+    const float* pr = g.gu_part + sp * g.gu_plane + (size_t)row * 2 * hstride + f8;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      gs[q] += *reinterpret_cast<const f32x4*>(pr + 4 * q);
+      us[q] += *reinterpret_cast<const f32x4*>(pr + hstride + 4 * q);
+    }
+  }
+  uint16_t hb[8], lb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float hv = swiglu(gs[e / 4][e % 4], us[e / 4][e % 4], lim);
+    hb[e] = f32_to_bf16_bits(hv);
+    lb[e] = f32_to_bf16_bits(hv - bf16_bits_to_f32(hb[e]));
+  }
+  const int hkb = hstride / 32, kb = f8 / 32, lane_hi = 16 * ((f8 % 32) / 8);
+  const int off = g.offsets[grp], rl = row - off;
+  const size_t prow = (size_t)16 * ((off + 15) / 16 + grp) + rl;
+  const size_t dst = ((prow / 16) * hkb + kb) * (kFragBytes / 2) + (prow % 16 + lane_hi) * 8;
+  *reinterpret_cast<u32x4*>(h + dst) = u32x4{hb[0] | (uint32_t)hb[1] << 16, hb[2] | (uint32_t)hb[3] << 16,
+                                             hb[4] | (uint32_t)hb[5] << 16, hb[6] | (uint32_t)hb[7] << 16};
+  if (shared && h_lo) {
+    const size_t dl = (((size_t)rl / 16) * hkb + kb) * (kFragBytes / 2) + (rl % 16 + lane_hi) * 8;
+    *reinterpret_cast<u32x4*>(h_lo + dl) = u32x4{lb[0] | (uint32_t)lb[1] << 16, lb[2] | (uint32_t)lb[3] << 16,
+                                                 lb[4] | (uint32_t)lb[5] << 16, lb[6] | (uint32_t)lb[7] << 16};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gateup_reduce(const GemmGeom& g, int rows, uint16_t* h, uint16_t* h_lo,
+                                int hstride, hipStream_t s) {
+  if (g.ksplit_gu < 2 || hstride % 32) return hipErrorInvalidValue;
+  const long threads = (long)rows * (hstride / 8);
+  dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  hipLaunchKernelGGL(gateup_reduce_kernel, grid, block, 0, s, g, rows, h, h_lo, hstride);
+  return hipGetLastError();
+}
 
 hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32_t* row_tok,
                                uint16_t* h, uint16_t* h_lo, int hstride, hipStream_t s) {
@@ -424,8 +518,10 @@ hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32
   if (tm != 128 && tm != 256) return hipErrorInvalidValue;
   const int wmax = g.I > g.Is ? g.I : g.Is;
   const int nblk = (2 * wmax + kTN - 1) / kTN;
+  const int ns = g.ksplit_gu < 1 ? 1 : g.ksplit_gu;
+  if ((g.H / 32) % (2 * ns) || (ns > 1 && !g.gu_part)) return hipErrorInvalidValue;
   const size_t items = (size_t)g.max_tiles * nblk;
-  dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds)), block(2 * tm);
+  dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds * ns)), block(2 * tm);
   if (tm == 256)
     hipLaunchKernelGGL((tiled_kernel<0, 256>), grid, block, 0, s, g, x, row_tok, h, hstride, h_lo,
                        nblk);

@@ -66,6 +66,13 @@ struct GemmGeom {
   // floats after plane s-1 (the combine adds the planes in order)
   int ksplit;
   size_t y_plane;
+  // LDS-tiled gate/up only: K split into ksplit_gu parts (each an even number
+  // of k-steps), part s writing fp32 partial sums of gate and up to
+  // gu_part + s * gu_plane, row r's gate at [2r][f], its up at [2r+1][f] (rows
+  // of 2 * hstride floats); launch_gateup_reduce then forms h
+  int ksplit_gu;
+  float* gu_part;
+  size_t gu_plane;
 };
 
 // h[row][f] = silu(x W_gate^T) * (x W_up^T) for every permuted row; h is fp32
@@ -94,6 +101,11 @@ hipError_t launch_gateup_tiled(const GemmGeom& g, const uint16_t* x, const int32
                                uint16_t* h, uint16_t* h_lo, int hstride, hipStream_t s);
 hipError_t launch_down_tiled(const GemmGeom& g, const uint16_t* h, const uint16_t* h_lo,
                              int hstride, float* y, hipStream_t s);
+// After a split-K gate/up: for each of the `rows` permuted rows, gate and up
+// summed over the parts in order, then h = SwiGLU written as
+// launch_gateup_tiled writes it (packed h, the shared group's remainder plane).
+hipError_t launch_gateup_reduce(const GemmGeom& g, int rows, uint16_t* h, uint16_t* h_lo,
+                                int hstride, hipStream_t s);
 
 // ---- combine: out[t] = Y[shared row of t] + sum_j w[t,j] Y[inv[t,j]] -------
 // Y may come in `planes` partial-sum planes, `plane` floats apart: each row is
