@@ -162,6 +162,39 @@ def test_concurrent_streams_one_handle():
         assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
 
 
+def test_concurrent_streams_share_the_second_stream():
+    """Two hot-expert batches (a router bias makes three of 64 experts hot)
+    on one handle, on two streams at once, each with its own workspace and
+    output: both put their LDS-tiled GEMMs on the handle's one second stream,
+    and each output equals, bit for bit, that batch's forward alone."""
+    s = W["tiny"].replace(name="tiny_bf16_hot_pair", act_dtype="bf16", experts=64, top_k=2,
+                          tokens=640)   # 256 + 384 tokens: 8 and 12 rows per expert, streaming
+    inp = moe_synth.make_layer(s, seed=5, device="cuda")
+    bias = torch.zeros(s.experts, device="cuda", dtype=torch.float32)
+    bias[:3] = 3.0
+    layer = make_layer(s)
+    layer.pack_inputs(inp)
+    xa, xb = inp.x[:256].contiguous(), inp.x[256:].contiguous()
+    ref_a, ra = layer.forward(xa, inp.router_w, bias, return_route=True)
+    ref_b, rb = layer.forward(xb, inp.router_w, bias, return_route=True)
+    torch.cuda.synchronize()
+    for r in (ra, rb):   # hot experts (LDS tiles on the second stream) and streaming ones
+        c = r.expert_counts.cpu().numpy()
+        assert (c[:3] >= 32).all() and (c[3:] < 32).all(), c
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        ws_a = torch.empty(layer.workspace_bytes(xa.shape[0]), dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(layer.workspace_bytes(xb.shape[0]), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            oa = layer.forward(xa, inp.router_w, bias, workspace=ws_a)
+        with torch.cuda.stream(s2):
+            ob = layer.forward(xb, inp.router_w, bias, workspace=ws_b)
+        torch.cuda.synchronize()
+        _say("concurrent hot batches", rep)
+        assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
+
+
 @pytest.mark.parametrize("tokens,experts", [(32, 16), (600, 16), (256, 64)])
 def test_graph_capture_replays(tokens, experts):
     """A forward captured in a HIP graph (no host synchronisation, no memset
