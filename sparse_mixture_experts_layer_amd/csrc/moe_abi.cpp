@@ -171,12 +171,13 @@ Plan make_plan(const moe_layer& L, int T) {
   // Streaming batches whose routing is uneven (a Zipf-popular expert can
   // take most of the tokens) would stream a hot expert's weights once per
   // 16-32-row tile: routed experts with kHotRows rows or more go to 128-row
-  // LDS tiles instead, in a launch after the streaming one.  The shared
-  // expert stays with the streaming GEMMs (a launch of its tiles alone would
-  // occupy a handful of CUs).  From 256 tokens: with Zipf-popular experts
-  // measured 6% faster at 256 tokens and 12% at 512, but 5% slower at 128,
-  // where the hot experts' few tiles leave the extra launch mostly idle;
-  // neutral on uniform routing.
+  // LDS tiles instead, launched on the handle's second stream beside the
+  // streaming GEMMs (see forward_impl).  The shared expert stays with the
+  // streaming GEMMs (a launch of its tiles alone would occupy a handful of
+  // CUs).  From 256 tokens: with Zipf-popular experts, as a launch after the
+  // streaming one, measured 6% faster at 256 tokens and 12% at 512 but 5%
+  // slower at 128, where the hot experts' few tiles leave that launch mostly
+  // idle; neutral on uniform routing.
   p.hybrid = !p.tiled && !p.large_dispatch && c.weight_dtype == MOE_BF16 &&
              c.act_dtype == MOE_BF16 && T >= kHybridMinTokens;
   p.hot = p.hybrid ? kHotRows : 0;
