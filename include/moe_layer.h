@@ -202,8 +202,10 @@ moe_status_t moe_layer_forward(moe_layer_t layer, int32_t num_tokens, const void
  * MOE_STAGE_EVENTS events created by the caller
  * (hipEventCreate or hipEventCreateWithFlags; events made with
  * hipEventDisableSystemFence only time the stages and skip the cache write-back
- * a default event's record performs, about 2 us each on a decode batch); the
- * same errors as moe_layer_forward, plus MOE_ERR_NULL for a NULL array. */
+ * a default event's record performs, about 2 us each on a decode batch); a
+ * NULL entry leaves that boundary unrecorded (to time one stage, pass its two
+ * events only).  The same errors as moe_layer_forward, plus MOE_ERR_NULL for
+ * a NULL array. */
 moe_status_t moe_layer_forward_timed(moe_layer_t layer, int32_t num_tokens, const void* x,
                                      const void* router_w, const float* router_bias,
                                      const void* packed, void* out, void* workspace,

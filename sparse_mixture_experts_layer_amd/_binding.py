@@ -120,7 +120,9 @@ class StageEvents:
     nothing about the visibility of the layer's outputs; synchronise the
     stream or device before reading them."""
 
-    def __init__(self, sets: int = 1):
+    def __init__(self, sets: int = 1, only=None):
+        """only: the stage boundaries to record (indices 0..MOE_STAGE_EVENTS-1),
+        all by default; the others stay NULL and are not recorded."""
         load()
         self.hip = C.CDLL("libamdhip64.so.7")
         self.hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
@@ -128,33 +130,39 @@ class StageEvents:
         self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
         self.hip.hipEventDestroy.argtypes = [C.c_void_p]
         self.sets = sets
+        self.only = tuple(range(MOE_STAGE_EVENTS)) if only is None else tuple(sorted(only))
         self.array = (C.c_void_p * (MOE_STAGE_EVENTS * sets))()
-        for i in range(MOE_STAGE_EVENTS * sets):
-            ev = C.c_void_p()
-            if self.hip.hipEventCreateWithFlags(C.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
-                raise RuntimeError("hipEventCreateWithFlags failed")
-            self.array[i] = ev
+        for s in range(sets):
+            for i in self.only:
+                ev = C.c_void_p()
+                if self.hip.hipEventCreateWithFlags(C.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                self.array[s * MOE_STAGE_EVENTS + i] = ev
 
     def ptr(self, s: int = 0) -> int:
         """Address of event set s (a hipEvent_t[MOE_STAGE_EVENTS])."""
         return C.addressof(self.array) + s * MOE_STAGE_EVENTS * C.sizeof(C.c_void_p)
 
-    def stage_ms(self, s: int = 0):
-        """Durations (ms) of the 5 stages recorded in set s (synchronises)."""
+    def elapsed_ms(self, s: int, a: int, b: int) -> float:
+        """Time (ms) from boundary a to boundary b of set s (synchronises)."""
         base = s * MOE_STAGE_EVENTS
-        self.hip.hipEventSynchronize(self.array[base + MOE_STAGE_EVENTS - 1])
-        out = []
-        for i in range(MOE_STAGE_EVENTS - 1):
-            ms = C.c_float()
-            if self.hip.hipEventElapsedTime(C.byref(ms), self.array[base + i],
-                                            self.array[base + i + 1]) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            out.append(ms.value)
-        return out
+        self.hip.hipEventSynchronize(self.array[base + b])
+        ms = C.c_float()
+        if self.hip.hipEventElapsedTime(C.byref(ms), self.array[base + a],
+                                        self.array[base + b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def stage_ms(self, s: int = 0):
+        """Durations (ms) of the 5 stages recorded in set s (synchronises);
+        None for a stage whose boundaries were not both recorded."""
+        return [self.elapsed_ms(s, i, i + 1) if i in self.only and i + 1 in self.only else None
+                for i in range(MOE_STAGE_EVENTS - 1)]
 
     def __del__(self):
         try:
             for i in range(MOE_STAGE_EVENTS * self.sets):
-                self.hip.hipEventDestroy(self.array[i])
+                if self.array[i]:
+                    self.hip.hipEventDestroy(self.array[i])
         except Exception:
             pass

@@ -422,7 +422,10 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   const bool int4 = c.weight_dtype == MOE_INT4_G32;
   const int E = c.num_experts, H = c.hidden, k = c.top_k;
 
-  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  // stage boundary i (a NULL entry of the caller's array: not recorded)
+  auto mark = [&](int i) -> hipError_t {
+    return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess;
+  };
   // up to 1024 tokens, top-k and dispatch run as one launch (the router stage
   // then ends after the logits); larger batches use the multi-workgroup
   // dispatch after a separate top-k

@@ -255,6 +255,14 @@ def test_timed_forward_matches(tokens):
         ms = ev.stage_ms(i)
         assert len(ms) == len(B.STAGES) == 5
         assert all(np.isfinite(v) and v > 0 for v in ms), ms
+    # only the gate/up stage's two boundaries recorded (NULL entries elsewhere)
+    gu = B.STAGES.index("gate_up")
+    part = B.StageEvents(sets=1, only=(gu, gu + 1))
+    out = layer.forward(inp.x, inp.router_w, stage_events=part)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    ms = part.stage_ms(0)
+    assert ms[gu] is not None and ms[gu] > 0 and all(v is None for j, v in enumerate(ms) if j != gu)
 
 
 def test_argument_errors():
