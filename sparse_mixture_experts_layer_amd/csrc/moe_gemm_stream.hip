@@ -452,9 +452,9 @@ hipError_t launch_mode(const GemmGeom& g, bool int4, bool act_f32, const void* a
     return hipGetLastError();
   } else {
     // down: k-steps per group U must divide every group's K/32 (the expert
-    // widths are only multiples of 32): 2 when even; 4 when divisible by 4 on
-    // the decode-sized launch (twice the bytes in flight per wave at two
-    // waves per SIMD measured slightly faster there)
+    // widths are only multiples of 32): 4 when divisible by 4 (twice the bytes
+    // in flight per wave: 0.5% on the decode-sized launch, 1.6% on the
+    // 32-row-tile one of the verify batch), else 2 when even
     const bool even = (g.I / 32) % 2 == 0 && (g.Is / 32) % 2 == 0;
     const bool quad = (g.I / 32) % 4 == 0 && (g.Is / 32) % 4 == 0;
     const int nsh = g.shared_tiles;
@@ -470,11 +470,13 @@ hipError_t launch_mode(const GemmGeom& g, bool int4, bool act_f32, const void* a
       else MOE_L(grid, MODE, false, TG, 1, 3);
       return hipGetLastError();
     } else {
-      if (even) MOE_L(grid, MODE, false, TG, 2, 1);
+      if (quad) MOE_L(grid, MODE, false, TG, 4, 1);
+      else if (even) MOE_L(grid, MODE, false, TG, 2, 1);
       else MOE_L(grid, MODE, false, TG, 1, 1);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || nsh == 0) return e;
-      if (even) MOE_L(grid_sh, MODE, false, TG, 2, 2);
+      if (quad) MOE_L(grid_sh, MODE, false, TG, 4, 2);
+      else if (even) MOE_L(grid_sh, MODE, false, TG, 2, 2);
       else MOE_L(grid_sh, MODE, false, TG, 1, 2);
       return hipGetLastError();
     }
