@@ -501,6 +501,21 @@ def test_next_row_workloads(name, sampled):
     _run(s, sample=_spread(s.tokens, sampled) if sampled else None)
 
 
+def test_page_router_selection_only_bias():
+    """The page's router configuration at the full shape with the other
+    reading of the router bias: it shifts the selection scores only, the
+    weights come from the unbiased sigmoid scores."""
+    s = W["page_router_decode"].replace(name="page_router_select", bias_mode="select")
+    _run(s)
+
+
+def test_dense_ffn_int4_decode():
+    """The dense FFN as one expert with INT4-g32 weights at a decode batch:
+    one expert of width 11264 through the INT4 streaming kernels."""
+    s = W["dense_decode"].replace(name="dense_int4", weight_dtype="int4_g32")
+    _run(s)
+
+
 # ----------------------------------------------------------------- SwiGLU limits
 
 LIMITS = dict(swiglu_limit=0.5, swiglu_limit_shared=0.75)   # act on N(0, 1) projections
