@@ -32,7 +32,9 @@ design notes):
   parameter count; gating is implied by the swiglu_limits fields, whose value
   is 0 (no clamp) for every MoE layer.  A nonzero limit L (7 for the routed
   and 16 for the shared experts of the last layers) is read as clamping the
-  gate projection to at most L and the up projection to [-L, L].
+  gate projection to at most L and the up projection to [-L, L].  The pages
+  give the limit values only, so this clamp is parity unpinned: its pin checks
+  the reading by hand, nothing on the pages checks the reading.
 * No bias terms in the expert linears; the shared expert is added unweighted.
 * Router bias: added to the logits before selection and weighting
   (bias_mode="logit"); bias_mode="select" uses it for selection only.
