@@ -25,12 +25,15 @@
  *     N rows of K elements, the nn.Linear [out][in] order).
  *   - Device pointers must be 16-byte aligned.  The caller owns every device
  *     buffer (activations, router weights, packed weights, output, workspace);
- *     the library allocates no device memory.  A handle owns host state only.
+ *     the library allocates no device memory.  A handle owns host state (and
+ *     for some configurations one HIP stream, below).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream),
  *     which must belong to the handle's device (the call makes that device
  *     current while it enqueues and restores the caller's afterwards).
  *     Nothing synchronises the host, and a forward enqueues kernels only (no
- *     memset or copy nodes), so it can be captured in a HIP graph.
+ *     memset or copy nodes; with the second stream below, also the event
+ *     records and waits that fork and join it), so it can be captured in a HIP
+ *     graph.
  *   - Argument errors are detected before anything is enqueued and returned as
  *     a status; moe_last_error() then holds a message (per thread).  Launch
  *     failures return MOE_ERR_DEVICE.  Faults inside kernels surface at the
@@ -45,11 +48,10 @@
  *     them): forked from `stream` by an event after the dispatch and joined
  *     back before the combine, so they overlap the streaming GEMMs on
  *     `stream`.  The output is the same as with everything in order.
- *     Concurrent forwards on one
- *     handle share that stream (and serialise there); while a forward on a
- *     handle is being captured into a graph, the second stream is part of the
- *     capture, so no other forward on that handle may run until the capture
- *     ends.
+ *     Concurrent forwards on one handle share that stream (and serialise
+ *     there); while a forward on a handle is being captured into a graph, the
+ *     second stream is part of the capture, so no other forward on that handle
+ *     may run until the capture ends.
  */
 #ifndef MOE_LAYER_H
 #define MOE_LAYER_H
