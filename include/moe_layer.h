@@ -77,7 +77,7 @@ typedef enum {
   MOE_ERR_DTYPE = 3,       /* unsupported dtype / scoring / mode value */
   MOE_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 5,   /* workspace smaller than moe_layer_workspace_bytes() */
-  MOE_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  MOE_ERR_UNSUPPORTED = 6, /* a valid request the library does not implement */
   MOE_ERR_DEVICE = 7       /* no usable gfx950 device, or a HIP call failed */
 } moe_status_t;
 
