@@ -83,6 +83,21 @@ def test_tiny_sigmoid_router_with_bias(bias_mode):
     _say("ok", res)
 
 
+def test_tiny_sigmoid_without_renorm():
+    """Sigmoid scores without renormalisation: each weight is the selected
+    expert's sigmoid score times routed_scale."""
+    s = W["tiny"].replace(name="tiny_sigmoid_norenorm", renormalize=False, score="sigmoid",
+                          routed_scale=2.5)
+    _run(s)
+
+
+def test_int4_large_batch_sampled():
+    """INT4-g32 weights past 1024 tokens: the multi-workgroup dispatch and the
+    INT4 streaming kernels with 32-row tiles, full layer shape, sampled tokens."""
+    s = W["int4_decode"].replace(name="int4_1537", tokens=1537)
+    _run(s, sample=_spread(1537, 10))
+
+
 def test_tiny_int4():
     s = W["tiny"].replace(name="tiny_int4", act_dtype="bf16", weight_dtype="int4_g32", inter=128,
                           shared_inter=128)
