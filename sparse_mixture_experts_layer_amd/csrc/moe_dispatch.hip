@@ -191,7 +191,7 @@ __device__ __forceinline__ void dispatch_body(
 // waves' choices are in this XCD's L2), one thread releases them device-wide
 // and counts the workgroup; the thread that counts last acquires every
 // workgroup's choices for its own.
-template <int NW>
+template <int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
     const float* __restrict__ part, int ks, const float* __restrict__ bias, int bias_mode, int T,
     int E, int k, int score, int renorm, float scale, int32_t* __restrict__ idx,
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_tok) {
   __shared__ int last;
   const int t = blockIdx.x * NW + (threadIdx.x >> 6);
-  if (t < T) topk_token(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
+  if (t < T) topk_token<NS>(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
   __syncthreads();
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this XCD's L2 -> memory
@@ -383,12 +383,23 @@ hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, in
     return hipErrorInvalidValue;
   // 4 tokens per workgroup up to 256 tokens (the top-k waves spread over more
   // CUs), 16 above
-#define MOE_TD(NW)                                                                              \
-  hipLaunchKernelGGL(topk_dispatch_kernel<NW>, dim3((T + NW - 1) / NW), dim3(NW * 64), 0, s,  \
-                     part, ks, bias, bias_mode, T, E, k, score, renorm, scale, idx, w, gap, done, \
-                     has_shared, tl, counts, offsets, perm, inv, row_tok)
-  if (T <= 4 * kWave) MOE_TD(4);
-  else MOE_TD(kDispWaves);
+#define MOE_TD(NW, NS)                                                                          \
+  hipLaunchKernelGGL((topk_dispatch_kernel<NW, NS>), dim3((T + NW - 1) / NW), dim3(NW * 64), 0, \
+                     s, part, ks, bias, bias_mode, T, E, k, score, renorm, scale, idx, w, gap,    \
+                     done, has_shared, tl, counts, offsets, perm, inv, row_tok)
+#define MOE_TD_NS(NW)                    \
+  switch (topk_slots(E)) {               \
+    case 1: MOE_TD(NW, 1); break;        \
+    case 2: MOE_TD(NW, 2); break;        \
+    case 5: MOE_TD(NW, 5); break;        \
+    default: MOE_TD(NW, kMaxPerLane);    \
+  }
+  if (T <= 4 * kWave) {
+    MOE_TD_NS(4);
+  } else {
+    MOE_TD_NS(kDispWaves);
+  }
+#undef MOE_TD_NS
 #undef MOE_TD
   return hipGetLastError();
 }

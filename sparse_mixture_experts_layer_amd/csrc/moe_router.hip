@@ -259,13 +259,14 @@ __global__ __launch_bounds__(512, 1) void router_logits_lds_kernel(
 }
 
 // One wave per token.
+template <int NS>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ part, int ks, const float* __restrict__ bias, int bias_mode, int T,
     int E, int k, int score, int renorm, float scale, int32_t* __restrict__ idx,
     float* __restrict__ wout, float* __restrict__ gap) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
+  topk_token<NS>(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
 }
 
 }  // namespace
@@ -319,8 +320,16 @@ hipError_t launch_router_topk(const float* part, int ks, const float* bias, int 
                               int E, int k, int score, int renorm, float scale, int32_t* idx,
                               float* w, float* gap, hipStream_t s) {
   dim3 grid((T + 3) / 4), block(256);
-  hipLaunchKernelGGL(router_topk_kernel, grid, block, 0, s, part, ks, bias, bias_mode, T, E, k,
-                     score, renorm, scale, idx, w, gap);
+#define MOE_RT(NS)                                                                               \
+  hipLaunchKernelGGL((router_topk_kernel<NS>), grid, block, 0, s, part, ks, bias, bias_mode, T, E, \
+                     k, score, renorm, scale, idx, w, gap)
+  switch (topk_slots(E)) {
+    case 1: MOE_RT(1); break;
+    case 2: MOE_RT(2); break;
+    case 5: MOE_RT(5); break;
+    default: MOE_RT(kMaxPerLane);
+  }
+#undef MOE_RT
   return hipGetLastError();
 }
 

@@ -96,49 +96,55 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr int kMaxPerLane = kMaxExperts / kWave;  // 8
 
-// One wave selects for token t.  Expert e lives in lane e % 64, slot e / 64.
+// Expert slots per lane a layer of E experts needs, rounded up to a compiled
+// variant: 1, 2, 5 (up to 320 experts) or 8.
+inline int topk_slots(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : (E <= 320 ? 5 : kMaxPerLane)); }
+
+// One wave selects for token t.  Expert e lives in lane e % 64, slot e / 64
+// (NS slots per lane, NS * 64 >= E).
 // The logits are the sum of the ks K-slice partials part[s][t][e], added in
 // slice order.  Each round takes the wave-wide largest remaining key; the
 // owner lane retires it.  Writes idx[t][j], wout[t][j] (j in descending
 // order) and gap[t].
+template <int NS>
 __device__ __forceinline__ void topk_token(const float* __restrict__ part, int ks,
                                            const float* __restrict__ bias, int bias_mode, int T,
                                            int E, int k, int score, int renorm, float scale, int t,
                                            int32_t* __restrict__ idx, float* __restrict__ wout,
                                            float* __restrict__ gap) {
   const int lane = threadIdx.x & 63;
-  float lg[kMaxPerLane], v[kMaxPerLane];
-  unsigned long long key[kMaxPerLane];
+  float lg[NS], v[NS];
+  unsigned long long key[NS];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) v[i] = 0.f;
+  for (int i = 0; i < NS; ++i) v[i] = 0.f;
   // K-slice partial sums, added in slice order; 8 slices of loads in flight
   for (int s0 = 0; s0 < ks; s0 += 8) {
-    float ld[8][kMaxPerLane];
+    float ld[8][NS];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
+      for (int i = 0; i < NS; ++i) {
         const int e = lane + i * kWave;
         ld[u][i] = (s0 + u < ks && e < E) ? part[((size_t)(s0 + u) * T + t) * E + e] : 0.f;
       }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) v[i] += ld[u][i];
+      for (int i = 0; i < NS; ++i) v[i] += ld[u][i];
   }
   // bias of each slot: all loads first (clamped index), then their uses
-  float bv[kMaxPerLane];
+  float bv[NS];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) bv[i] = 0.f;
+  for (int i = 0; i < NS; ++i) bv[i] = 0.f;
   if (bias) {
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < NS; ++i) {
       const int e = lane + i * kWave;
       bv[i] = bias[e < E ? e : E - 1];
     }
   }
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NS; ++i) {
     const int e = lane + i * kWave;
     lg[i] = -INFINITY;
     key[i] = 0ull;  // below every real key
@@ -153,7 +159,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
   // softmax reference point: the largest logit (selection may use biased scores)
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) m = fmaxf(m, lg[i]);
+  for (int i = 0; i < NS; ++i) m = fmaxf(m, lg[i]);
   m = wave_max(m);
 
   float denom = 0.f, kth = 0.f;
@@ -162,7 +168,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
   for (int r = 0; r < k; ++r) {
     unsigned long long best = 0ull;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
+    for (int i = 0; i < NS; ++i) best = key[i] > best ? key[i] : best;
     best = wave_max_u64(best);
     // every lane holds the same best: make it scalar
     best = ((unsigned long long)__builtin_amdgcn_readfirstlane((uint32_t)(best >> 32)) << 32) |
@@ -171,12 +177,12 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
     const int owner = e & 63, slot = e >> 6;
     float l = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
+    for (int i = 0; i < NS; ++i)
       if (i == slot) l = lg[i];
     l = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(l), owner));
     if (lane == owner) {
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
+      for (int i = 0; i < NS; ++i)
         if (i == slot) key[i] = 0ull;
     }
     const float p = score == 0 ? expf(l - m) : 1.f / (1.f + expf(-l));
@@ -189,14 +195,14 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
   }
   unsigned long long nxt = 0ull;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) nxt = key[i] > nxt ? key[i] : nxt;
+  for (int i = 0; i < NS; ++i) nxt = key[i] > nxt ? key[i] : nxt;
   nxt = wave_max_u64(nxt);
 
   if (!renorm) {
     if (score == 0) {
       float z = 0.f;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
+      for (int i = 0; i < NS; ++i)
         if (lane + i * kWave < E) z += expf(lg[i] - m);
       denom = wave_sum(z);
     } else {
