@@ -394,6 +394,18 @@ def test_max_experts_and_top_k(tokens):
     _run(s)
 
 
+@pytest.mark.parametrize("tokens", [40, 1100])
+@pytest.mark.parametrize("experts", [65, 128, 129, 320, 321])
+def test_topk_slot_variants(experts, tokens):
+    """Expert counts at the edges of the compiled top-k variants (1, 2, 5 or 8
+    expert slots per lane, the smallest that holds E is launched), through the
+    fused top-k + dispatch launch (40 tokens) and the separate top-k launch
+    (1100 tokens)."""
+    s = W["tiny"].replace(name=f"slots_{experts}_{tokens}", act_dtype="bf16", experts=experts,
+                          top_k=8, tokens=tokens)
+    _run(s)
+
+
 # ----------------------------------------------------------------- full Step-3.5-Flash shapes
 
 def _spread(T, n, seed=0):
