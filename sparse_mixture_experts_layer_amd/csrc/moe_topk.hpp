@@ -170,9 +170,13 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
 #pragma unroll
     for (int i = 0; i < NS; ++i) best = key[i] > best ? key[i] : best;
     best = wave_max_u64(best);
-    // every lane holds the same best: make it scalar
-    best = ((unsigned long long)__builtin_amdgcn_readfirstlane((uint32_t)(best >> 32)) << 32) |
-           __builtin_amdgcn_readfirstlane((uint32_t)best);
+    // every lane holds the same best: make it scalar (the builtin returns a
+    // signed int: each half goes through uint32_t, or the low half -- whose
+    // top bit is set for every expert index -- would sign-extend over the
+    // score in the high half)
+    best = ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(best >> 32))
+            << 32) |
+           (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)best);
     const int e = (int)(0xffffffffu - (uint32_t)best);
     const int owner = e & 63, slot = e >> 6;
     float l = 0.f;
