@@ -234,7 +234,8 @@ def make_layer(shape: LayerShape, seed: int = 0, device="cpu",
 
 
 def host_f64(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
-    """Exact float64 host copy of a float tensor (bf16/f16/f32 widen exactly)."""
+    """Exact float64 host copy of a float tensor (bf16/f16/f32 widen exactly;
+    widened on the tensor's own device, then copied)."""
     if t is None:
         return None
-    return t.detach().to("cpu").to(torch.float64).numpy()
+    return t.detach().to(torch.float64).to("cpu").numpy()

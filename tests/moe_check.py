@@ -2,11 +2,19 @@
 compare it with the oracle element by element.
 
 Comparison rules (tolerances per output dtype):
-  * routing: the selected experts, in rank order, must equal the oracle's for
-    every token whose oracle k-th / (k+1)-th selection-score gap is >= 1e-4
-    (a smaller gap can flip under a different fp32 summation order);
+  * routing, over every token of the batch: the selected experts, in rank
+    order, must equal the oracle's for every token whose oracle k-th /
+    (k+1)-th selection-score gap is >= 1e-4 (a smaller gap can flip under a
+    different fp32 summation order); inside the selection, two ranks may
+    differ only where the oracle's scores of the two experts are within 1e-4
+    of each other (a swap of near-equal scores).  The gate weights of tokens
+    with the same selection agree within 1e-5, and the GPU's topk_gap agrees
+    with the oracle's gap on every token (fp32 logits summed in another
+    order: within 2e-4 x max(1, |k-th score|), far below the distance of two
+    neighbouring order statistics that an off-by-one would report);
   * dispatch: counts, offsets, perm and inv must equal the reference dispatch
-    of the GPU's own indices bit for bit;
+    of the GPU's own indices bit for bit -- and, where the GPU's routing equals
+    the oracle's on every token, that is the oracle's own dispatch;
   * outputs: max|y_gpu - y_ref| <= tol * RMS(y_ref) over the compared tokens,
     tol = 2e-2 for bf16 outputs, 5e-2 for INT4 weights, 1e-3 for fp32 outputs
     (split-bf16 operands leave a relative residual below 2^-16 per product and
@@ -15,12 +23,12 @@ Comparison rules (tolerances per output dtype):
     with the oracle re-run on the GPU's routing.
   * bf16 outputs carry their own rounding, up to 2^-8 |y| per element, which no
     kernel can avoid; where a shape's largest |y| is ~5x RMS that alone is
-    ~2e-2 RMS, and where h is rounded to bf16 (the large-batch path) that
-    rounding adds up to ~1.3e-2 RMS on layers without a shared expert.  Shapes
-    outside the five workloads (small edge cases) therefore assert the
-    rounding-aware form: max_i (|err_i| - 2^-8 |y_ref_i|) <= tol * RMS, the
-    stated budget applied to the error beyond the output's own rounding; the
-    plain figure is still reported.  Indexing mistakes (a wrong row, expert or
+    ~2e-2 RMS.  For shapes outside the benchmarked workloads (small edge
+    cases), when that floor (max|bf16(y_ref) - y_ref| / RMS) is 1e-2 or more,
+    the rounding-aware form max_i (|err_i| - 2^-8 |y_ref_i|) <= tol * RMS is
+    asserted instead -- the stated budget applied to the error beyond the
+    output's own rounding; below 1e-2 the plain form is asserted everywhere.
+    Both figures are reported.  Indexing mistakes (a wrong row, expert or
     tile, a dropped k-step) give errors of order RMS and fail either form.
 """
 from __future__ import annotations
@@ -32,6 +40,8 @@ import moe_synth
 import oracle
 
 NEAR_TIE = 1e-4
+GAP_RTOL = 2e-4
+RELAXED_FLOOR = 1e-2
 
 
 def out_tolerance(shape) -> float:
@@ -41,8 +51,9 @@ def out_tolerance(shape) -> float:
 
 
 def expert_loader(inp):
-    """e -> (W_gate, W_up, W_down) float64 host arrays of one expert (group
-    e == E is the shared expert)."""
+    """e -> (W_gate, W_up, W_down) float64 host arrays of one expert, read from
+    the device each call (nothing is kept: a full-shape layer is 9 GB of bf16);
+    and the shared expert's, or None."""
     if inp.shape.weight_dtype == "int4_g32":
         q = inp.q
 
@@ -72,6 +83,58 @@ def run_gpu(layer, inp, tokens=None, seed_ws=None):
     return out, route
 
 
+def oracle_routing(inp, T, k, score, renormalize, routed_scale, bias_mode, chunk=8192):
+    """The oracle's routing of tokens 0..T-1, computed in chunks of tokens (the
+    logits of a token do not depend on the others): idx [T][k], w [T][k],
+    gap [T] and the selection scores [T][E] (float32)."""
+    wr = moe_synth.host_f64(inp.router_w)
+    bias = None if inp.router_bias is None else inp.router_bias.cpu().numpy()
+    idx, w, gap, sel = [], [], [], []
+    for t0 in range(0, T, chunk):
+        x64 = moe_synth.host_f64(inp.x[t0:min(T, t0 + chunk)])
+        i, ww, l32 = oracle.route(x64, wr, bias, k, score, renormalize, routed_scale, bias_mode)
+        s = l32
+        if bias is not None and bias_mode == "select":
+            s = (l32.astype(np.float64) + bias[None, :]).astype(np.float32)
+        idx.append(i)
+        w.append(ww)
+        gap.append(oracle.topk_gap(s, k))
+        sel.append(s)
+    return (np.concatenate(idx), np.concatenate(w), np.concatenate(gap), np.concatenate(sel))
+
+
+def tile_edge_tokens(route, k, heights=(128, 256), tiles_per_group=None, T=None, seed=0):
+    """Tokens at the first and last row of every m-tile of every group (each
+    routed expert, and the shared expert over all T tokens), for each tile
+    height, read off the GPU's own bit-checked dispatch: together they reach
+    every tile of both tiled GEMMs, every ragged group tail and the last shared
+    tile.  tiles_per_group limits the m-tiles per group to the first, the last
+    and that many more drawn at random."""
+    rng = np.random.default_rng(seed)
+    counts = route.expert_counts.cpu().numpy().astype(np.int64)
+    offsets = route.expert_offsets.cpu().numpy().astype(np.int64)
+    perm = route.perm.cpu().numpy().astype(np.int64)
+    toks = set()
+
+    def edges(count, pick):
+        for bm in heights:
+            nt = (count + bm - 1) // bm
+            ms = range(nt)
+            if tiles_per_group is not None and nt > tiles_per_group + 2:
+                ms = sorted({0, nt - 1} | set(rng.choice(np.arange(1, nt - 1), tiles_per_group,
+                                                         replace=False).tolist()))
+            for m in ms:
+                pick(m * bm)
+                pick(min((m + 1) * bm, count) - 1)
+
+    for e in range(len(counts)):
+        if counts[e]:
+            edges(int(counts[e]), lambda r, e=e: toks.add(int(perm[offsets[e] + r]) // k))
+    if T is not None:   # the shared group: row r is token r
+        edges(T, lambda r: toks.add(int(r)))
+    return sorted(toks)
+
+
 def compare(inp, out, route, sample=None, score=None, renormalize=None, routed_scale=None,
             bias_mode=None, k=None, tokens=None, strict=True):
     """Checks one GPU forward against the oracle; returns a dict of figures.
@@ -83,73 +146,87 @@ def compare(inp, out, route, sample=None, score=None, renormalize=None, routed_s
     routed_scale = shape.routed_scale if routed_scale is None else routed_scale
     bias_mode = shape.bias_mode if bias_mode is None else bias_mode
     T = out.shape[0]
-    x64 = moe_synth.host_f64(inp.x[:T])
     wr = moe_synth.host_f64(inp.router_w)
     bias = None if inp.router_bias is None else inp.router_bias.cpu().numpy()
     g_idx = route.topk_idx.cpu().numpy().astype(np.int64)
     g_w = route.topk_w.cpu().numpy().astype(np.float64)
+    g_gap = route.topk_gap.cpu().numpy().astype(np.float64)
     E = shape.experts
+    if getattr(route, "debug_flag", None) is not None:   # an index-checking build
+        flag = route.debug_flag.cpu().numpy()
+        assert (flag == 0).all(), f"a kernel read an out-of-range index: kind {flag[0]}, value {flag[1]}"
 
-    # dispatch: bit-exact against the reference dispatch of the GPU's own routing
-    counts, offsets, perm, inv = oracle.dispatch(g_idx, E)
+    # routing of every token, in rank order
+    o_idx, o_w, o_gap, sel = oracle_routing(inp, T, k, score, renormalize, routed_scale, bias_mode)
+    exempt = o_gap < NEAR_TIE
+    same_set = (np.sort(g_idx, axis=1) == np.sort(o_idx, axis=1)).all(axis=1)
+    bad = ~same_set & ~exempt
+    assert not bad.any(), (f"routing differs on {bad.sum()} non-near-tie tokens, e.g. token "
+                           f"{np.argmax(bad)}: gpu {g_idx[bad][0]} oracle {o_idx[bad][0]}")
+    s_g = np.take_along_axis(sel.astype(np.float64), g_idx, axis=1)
+    s_o = np.take_along_axis(sel.astype(np.float64), o_idx, axis=1)
+    swap = (g_idx != o_idx) & same_set[:, None]
+    far = swap & (np.abs(s_g - s_o) >= NEAR_TIE)
+    assert not far.any(), (f"rank order differs beyond near-equal scores on token "
+                           f"{np.argmax(far.any(axis=1))}")
+    identical = (g_idx == o_idx).all(axis=1)
+    # gate weights of tokens with the same selection, matched by expert
+    g_ord = np.argsort(g_idx, axis=1, kind="stable")
+    o_ord = np.argsort(o_idx, axis=1, kind="stable")
+    gw_s = np.take_along_axis(g_w, g_ord, axis=1)
+    ow_s = np.take_along_axis(o_w, o_ord, axis=1)
+    werr = float(np.abs(gw_s[same_set] - ow_s[same_set]).max()) if same_set.any() else 0.0
+    assert werr <= 1e-5, f"gate weights differ by {werr}"
+    # the k-th / (k+1)-th gap the GPU reports
+    kth = np.abs(np.sort(sel.astype(np.float64), axis=1)[:, ::-1][:, k - 1])
+    fin = np.isfinite(o_gap)
+    assert (np.isfinite(g_gap) == fin).all(), "topk_gap: +inf where k < E, or finite where k == E"
+    gerr = np.abs(g_gap[fin] - o_gap[fin]) / np.maximum(1.0, kth[fin]) if fin.any() else np.zeros(1)
+    assert gerr.max() <= GAP_RTOL, f"topk_gap differs by {gerr.max():.3g} x max(1, |k-th score|)"
+
+    # dispatch: bit-exact against the reference dispatch of the GPU's routing,
+    # which is the oracle's routing on every token when all are identical
+    all_identical = bool(identical.all())
+    counts, offsets, perm, inv = oracle.dispatch(o_idx if all_identical else g_idx, E)
     assert np.array_equal(route.expert_counts.cpu().numpy(), counts), "expert counts differ"
     assert np.array_equal(route.expert_offsets.cpu().numpy(), offsets), "expert offsets differ"
     assert np.array_equal(route.perm.cpu().numpy(), perm), "permutation differs"
     assert np.array_equal(route.inv.cpu().numpy(), inv), "inverse permutation differs"
 
-    rows = np.arange(T) if sample is None else np.asarray(sample)
+    # outputs of the compared tokens
+    rows = np.arange(T) if sample is None else np.asarray(sorted(set(int(r) for r in sample)))
+    x64 = moe_synth.host_f64(inp.x[torch.as_tensor(rows, device=inp.x.device)])
     load, shared = expert_loader(inp)
-    cache = {}
-
-    def experts(e):
-        if e not in cache:
-            cache[e] = load(e)
-        return cache[e]
-
     lims = dict(swiglu_limit=shape.swiglu_limit, swiglu_limit_shared=shape.swiglu_limit_shared)
-    y_ref, o_idx, o_w, l32 = oracle.forward(x64[rows], wr, bias, experts, shared, k, score,
-                                            renormalize, routed_scale, bias_mode, **lims)
-    sel_scores = l32
-    if bias is not None and bias_mode == "select":
-        sel_scores = (l32.astype(np.float64) + bias[None, :]).astype(np.float32)
-    gap = oracle.topk_gap(sel_scores, k)
-    exempt = gap < NEAR_TIE
-    # sets are compared; the rank order inside a set may flip on equal-ish logits
-    g_ord = np.argsort(g_idx[rows], axis=1, kind="stable")
-    o_ord = np.argsort(o_idx, axis=1, kind="stable")
-    g_sorted = np.take_along_axis(g_idx[rows], g_ord, axis=1)
-    o_sorted = np.take_along_axis(o_idx, o_ord, axis=1)
-    same = (g_sorted == o_sorted).all(axis=1)
-    bad = ~same & ~exempt
-    assert not bad.any(), (f"routing differs on {bad.sum()} non-near-tie tokens, e.g. token "
-                           f"{rows[np.argmax(bad)]}: gpu {g_idx[rows][bad][0]} oracle {o_idx[bad][0]}")
-    # weights of identically routed tokens
-    gw_s = np.take_along_axis(g_w[rows], g_ord, axis=1)
-    ow_s = np.take_along_axis(o_w, o_ord, axis=1)
-    werr = np.abs(gw_s[same] - ow_s[same]).max() if same.any() else 0.0
-    assert werr <= 1e-5, f"gate weights differ by {werr}"
-    # tokens routed differently inside the near-tie band: oracle on the GPU's routing
-    flip = ~same
-    if flip.any():
-        y_f, *_ = oracle.forward(x64[rows][flip], wr, bias, experts, shared, k, score,
-                                 renormalize, routed_scale, bias_mode, force_idx=g_idx[rows][flip],
-                                 **lims)
-        y_ref = y_ref.copy()
-        y_ref[flip] = y_f
+    flip = ~same_set[rows]
+    # the oracle on its own routing; tokens routed differently inside the
+    # near-tie band: the oracle on the GPU's routing
+    force = np.where(flip[:, None], g_idx[rows], o_idx[rows])
+    y_ref, *_ = oracle.forward(x64, wr, bias, load, shared, k, score, renormalize, routed_scale,
+                               bias_mode, force_idx=force, **lims)
     y_gpu = out[torch.as_tensor(rows, device=out.device)].double().cpu().numpy()
     rms = float(np.sqrt(np.mean(y_ref ** 2)))
     err = float(np.abs(y_gpu - y_ref).max())
     tol = out_tolerance(shape)
-    res = {"max_err_over_rms": err / rms, "rms": rms, "tol": tol, "near_tie_tokens": int(exempt.sum()),
-           "flipped": int(flip.sum()), "compared_tokens": len(rows), "weight_err": float(werr)}
+    res = {"max_err_over_rms": err / rms, "rms": rms, "tol": tol,
+           "near_tie_tokens": int(exempt.sum()), "flipped": int((~same_set).sum()),
+           "rank_swaps": int(swap.sum()), "routing_identical": all_identical,
+           "compared_tokens": len(rows), "weight_err": werr,
+           "gap_err_rel": float(gerr.max())}
+    plain_ok = err <= tol * rms
+    res["plain_ok"] = bool(plain_ok)
+    floor = 0.0
     if out.dtype == torch.bfloat16:
         y_rounded = torch.from_numpy(y_ref).to(torch.bfloat16).double().numpy()
-        res["out_rounding_floor"] = float(np.abs(y_rounded - y_ref).max()) / rms
+        floor = float(np.abs(y_rounded - y_ref).max()) / rms
+        res["out_rounding_floor"] = floor
         excess = float((np.abs(y_gpu - y_ref) - 2.0 ** -8 * np.abs(y_ref)).max())
         res["excess_over_rounding"] = excess / rms
-    if strict or out.dtype != torch.bfloat16:
-        assert err <= tol * rms, f"output error {err / rms:.4g} x RMS exceeds {tol}: {res}"
+    if strict or out.dtype != torch.bfloat16 or floor < RELAXED_FLOOR:
+        res["bar"] = "plain"
+        assert plain_ok, f"output error {err / rms:.4g} x RMS exceeds {tol}: {res}"
     else:
+        res["bar"] = "rounding-aware"
         assert excess <= tol * rms, (f"error beyond the output rounding "
                                      f"{excess / rms:.4g} x RMS exceeds {tol}: {res}")
     return res

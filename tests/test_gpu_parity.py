@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import moe_synth
-from moe_check import compare, make_layer, run_gpu
+from moe_check import compare, make_layer, run_gpu, tile_edge_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -20,9 +20,12 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _run(shape, seed=0, tokens=None, max_tokens=None, layer_kw=None, cmp_kw=None, sample=None):
-    """Runs one case; shapes other than the five workloads use the
-    rounding-aware output check (see moe_check)."""
+def _run(shape, seed=0, tokens=None, max_tokens=None, layer_kw=None, cmp_kw=None, sample=None,
+         edges=None):
+    """Runs one case; shapes other than the benchmarked workloads may use the
+    rounding-aware output check (see moe_check).  edges: also compare the
+    tokens at the first and last row of every m-tile of every group (a dict of
+    tile_edge_tokens arguments), read off the GPU's own dispatch."""
     cmp_kw = dict(cmp_kw or {})
     cmp_kw.setdefault("strict", shape.name in W)
     _say(shape.name, f"seed={seed}", f"tokens={tokens or shape.tokens}", layer_kw or "")
@@ -31,6 +34,12 @@ def _run(shape, seed=0, tokens=None, max_tokens=None, layer_kw=None, cmp_kw=None
     layer = make_layer(shape, max_tokens=max_tokens or shape.tokens, **(layer_kw or {}))
     layer.pack_inputs(inp)
     out, route = run_gpu(layer, inp, tokens)
+    if edges is not None:
+        T = out.shape[0]
+        sh = T if shape.shared_inter else None
+        sample = sorted(set(sample or []) | set(tile_edge_tokens(route, shape.top_k, T=sh,
+                                                                 **edges)))
+        _say("tile-edge sample", len(sample), "tokens")
     res = compare(inp, out, route, sample=sample, **cmp_kw)
     _say("ok", res)
     return inp, layer, out, route, res
@@ -121,11 +130,17 @@ def test_exact_ties_go_to_lower_index():
     layer.pack_inputs(inp)
     out, route = run_gpu(layer, inp)
     idx = route.topk_idx.cpu().numpy()
+    both_seen = 0
     for a, b in [(1, 9), (3, 4), (0, 15), (7, 12)]:
         has_a = (idx == a).any(axis=1)
         has_b = (idx == b).any(axis=1)
         assert not (has_b & ~has_a).any(), f"expert {b} chosen over its twin {a}"
-    assert (has_a | has_b).any()
+        both = has_a & has_b   # both twins selected: the lower one ranks first
+        ja = np.argmax(idx == a, axis=1)
+        jb = np.argmax(idx == b, axis=1)
+        assert (ja[both] < jb[both]).all(), f"twin {b} ranked before {a}"
+        both_seen += int(both.sum())
+    assert both_seen > 0
     compare(inp, out, route)
 
 
@@ -419,7 +434,7 @@ def test_decode_32():
 
 
 def test_verify_256_zipf():
-    _, _, _, route, _ = _run(W["verify"], sample=_spread(256, 40))
+    _, _, _, route, _ = _run(W["verify"])
     counts = route.expert_counts.cpu().numpy()
     assert counts.max() > 150 and (counts > 0).sum() > 200   # skewed and wide
 
@@ -451,7 +466,11 @@ def test_batch_sizes_around_the_second_stream(tokens):
 
 
 def test_prefill_16384_sampled():
-    _run(W["prefill"], sample=_spread(16384, 24))
+    """Every token at the first or last row of a 128-row and of a 256-row
+    m-tile of every expert and of the shared expert (what both tiled GEMMs
+    cover: every tile, ragged group tails, the last shared tile), plus a
+    spread of others."""
+    _run(W["prefill"], sample=_spread(16384, 24), edges={})
 
 
 def test_max_tokens_sampled():
@@ -461,7 +480,8 @@ def test_max_tokens_sampled():
     sampled tokens (the first, middle and last among them)."""
     T = 1 << 18
     s = W["prefill"].replace(name="max_tokens", tokens=T)
-    _run(s, sample=_spread(T, 16), cmp_kw={"strict": True})
+    _run(s, sample=_spread(T, 16), cmp_kw={"strict": True},
+         edges={"heights": (256,), "tiles_per_group": 1})
 
 
 def test_int4_decode_32():
@@ -481,7 +501,7 @@ def test_mid_size_batches_sampled(tokens):
     dispatch: 64 tokens per dispatching wave), 1025 (first size on the
     multi-workgroup dispatch)."""
     s = W["decode"].replace(name=f"mid_{tokens}", tokens=tokens)
-    _run(s, sample=_spread(tokens, 10))
+    _run(s, sample=_spread(tokens, 10), edges={"heights": (128,)} if tokens >= 1024 else None)
 
 
 def test_int4_two_token_groups_sampled():
@@ -505,7 +525,7 @@ def test_step3_shape_decode():
 
 def test_step3_shape_large_batch_sampled():
     s = STEP3.replace(name="step3_batch", tokens=1024)      # 64 rows per expert: tiled path
-    _run(s, cmp_kw=dict(renormalize=False), sample=_spread(1024, 12))
+    _run(s, cmp_kw=dict(renormalize=False), sample=_spread(1024, 12), edges={"heights": (128,)})
 
 
 @pytest.mark.parametrize("tokens", [32, 512])

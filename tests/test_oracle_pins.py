@@ -259,7 +259,38 @@ def check_swiglu_limit():
     assert y[0, 0] == pytest.approx(silu(10.0) * 10.0 + silu(7.0) * 7.0, rel=1e-14)
 
 
-PINS = [check_hand_case, check_topk_bruteforce, check_weights_closed_form,
+def check_topk_gap_bruteforce():
+    """topk_gap = (k-th - (k+1)-th) largest selection score per token, by a
+    full sort written out per row; +inf when k equals the number of experts;
+    exact ties give 0; the gap is the one at the selection boundary (a brute
+    force over every expert of the selected and the rejected set)."""
+    rng = _rng(9)
+    for trial in range(60):
+        t, e = int(rng.integers(1, 7)), int(rng.integers(2, 24))
+        k = int(rng.integers(1, e + 1))
+        s = rng.standard_normal((t, e)).astype(np.float32)
+        if trial % 3 == 0:
+            s = np.round(s * 2).astype(np.float32)       # many exact ties
+        gap = oracle.topk_gap(s, k)
+        for r in range(t):
+            vals = sorted((float(v) for v in s[r]), reverse=True)
+            want = math.inf if k == e else vals[k - 1] - vals[k]
+            assert gap[r] == want, (trial, r, gap[r], want)
+            if k < e:   # smallest selected minus largest rejected score
+                sel = oracle.select_topk(s[r:r + 1], k)[0]
+                rest = np.setdiff1d(np.arange(e), sel)
+                assert gap[r] == float(s[r, sel].min()) - float(s[r, rest].max())
+    # an exact tie at the boundary (experts 2 and 3 for k = 2): gap 0, and the
+    # selection is still defined (the lower index); one past it (k = 3): gap 1
+    s = np.array([[3.0, 1.0, 2.0, 2.0, 0.5]], np.float32)
+    assert oracle.topk_gap(s, 2)[0] == 0.0 and oracle.topk_gap(s, 3)[0] == 1.0
+    assert oracle.select_topk(s, 2)[0].tolist() == [0, 2]
+    assert oracle.topk_gap(s, 1)[0] == 1.0 and oracle.topk_gap(s, 4)[0] == 0.5
+    assert oracle.topk_gap(s, 5)[0] == math.inf
+
+
+PINS = [check_hand_case, check_topk_bruteforce, check_topk_gap_bruteforce,
+        check_weights_closed_form,
         check_identical_experts_dense, check_single_expert_contribution,
         check_relabel_and_token_independence, check_router_bias_and_fp32_logits,
         check_dispatch, check_int4, check_parameter_count, check_swiglu_limit]
@@ -357,10 +388,28 @@ def _mut_limit_shared_uses_routed(m):
     m.forward = fwd
 
 
+def _mut_gap_off_by_one(m):
+    def gap(scores32, k):
+        s = np.sort(np.asarray(scores32, np.float64), axis=1)[:, ::-1]
+        if k + 1 >= s.shape[1]:
+            return np.full(s.shape[0], np.inf)
+        return s[:, k] - s[:, k + 1]          # the (k+1)-th and (k+2)-th scores
+    m.topk_gap = gap
+
+
+def _mut_gap_ascending(m):
+    def gap(scores32, k):
+        s = np.sort(np.asarray(scores32, np.float64), axis=1)
+        if k >= s.shape[1]:
+            return np.full(s.shape[0], np.inf)
+        return s[:, k] - s[:, k - 1]          # gap among the k smallest
+    m.topk_gap = gap
+
+
 MUTATIONS = [_mut_swap_gate_up, _mut_no_renorm, _mut_tie_high_index, _mut_silu_sign,
              _mut_down_transposed, _mut_softmax_no_max_shift_wrong, _mut_shared_weighted,
              _mut_int4_high_nibble_first, _mut_dispatch_unstable, _mut_limit_gate_only,
-             _mut_limit_shared_uses_routed]
+             _mut_limit_shared_uses_routed, _mut_gap_off_by_one, _mut_gap_ascending]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
