@@ -70,6 +70,9 @@ def parse():
                     help="skip timing the oracle on the host (e.g. under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the default decode workload: skip the prefill leg (16384 tokens) "
+                         "that the line otherwise carries as its 'prefill' object")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
@@ -178,35 +181,47 @@ def cpu_baseline(inp, shape, target_s: float):
         s = min(T, s * 2 if elapsed < target_s / 4 else max(s + 1, int(s * target_s / elapsed)))
         host.clear()
     return {"value": s / elapsed, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"first {s} of the {T} tokens of the same batch (float64 NumPy oracle, "
                       f"{elapsed:.1f} s; expert weights widened one expert at a time)"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the layer's multi-GPU sharding is designed, not built).", file=sys.stderr)
-        sys.exit(2)
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or 'unknown'."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+WL_DESC = {"tiny": "tiny parity layer", "decode": "Step-3.5-Flash MoE layer, decode batch",
+           "verify": "Step-3.5-Flash MoE layer, MTP verify batch (64 streams x 4), Zipf experts",
+           "prefill": "Step-3.5-Flash MoE layer, prefill chunk",
+           "int4_decode": "Step-3.5-Flash MoE layer, decode batch, INT4-g32 weights",
+           "mtp_decode": "Step-3.5-Flash last MoE layer (SwiGLU limits 7 / 16), decode batch",
+           "page_router_decode": "Step-3.5-Flash MoE layer under the page's router config "
+                                 "(sigmoid, router bias, x3), decode batch",
+           "step3_decode": "Step-3 MoE layer shape, decode batch",
+           "step3_prefill": "Step-3 MoE layer shape, 4096-token chunk",
+           "dense_decode": "dense SwiGLU FFN (width 11264) as one expert, decode batch",
+           "dense_prefill": "dense SwiGLU FFN (width 11264) as one expert, prefill chunk"}
+
+
+def measure(workload: str, args, cpu_seconds: float) -> dict:
+    """Times one workload (W warm-up steps, then K steps between two device
+    synchronisations) and returns its JSON fields."""
     import torch
-    if args.copy_calibration:
-        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")
-        src.fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copied {args.copy_calibration} bytes 5 times")
-        return
     import moe_synth
     from sparse_mixture_experts_layer_amd import _binding as B
     from sparse_mixture_experts_layer_amd.layer import MoELayer
 
-    shape = moe_synth.WORKLOADS[args.workload]
+    shape = moe_synth.WORKLOADS[workload]
     T, H, E, k, I, Is = (shape.tokens, shape.hidden, shape.experts, shape.top_k, shape.inter,
                          shape.shared_inter)
-    log(f"[bench] workload {args.workload}: T={T} H={H} E={E} k={k} I={I} Is={Is} "
+    log(f"[bench] workload {workload}: T={T} H={H} E={E} k={k} I={I} Is={Is} "
         f"weights={shape.weight_dtype}")
     t0 = time.time()
     inp = moe_synth.make_layer(shape, seed=args.seed, device="cuda")
@@ -243,7 +258,8 @@ def main():
     torch.cuda.synchronize()
     stages = [ev_all.stage_ms(i) for i in range(nb)]
     stage_avg = [sum(s[j] for s in stages) / len(stages) for j in range(len(B.STAGES))]
-    log(f"[bench] gate_up ms (timed region): {gu_ms:.4f}; stage ms (separate pass): "
+    log(f"[bench] {workload}: {ms:.4f} ms/step; gate_up ms (timed region): {gu_ms:.4f}; "
+        "stage ms (separate pass): "
         + ", ".join(f"{n}={v:.4f}" for n, v in zip(B.STAGES, stage_avg)))
 
     # routing of the (deterministic) batch: distinct experts touched
@@ -260,12 +276,12 @@ def main():
     f_alg = T * (2 * H * E + k * 6 * H * I + 6 * H * Is)
     t_layer = ms / 1e3
     Us = U
-    if args.workload in MFMA_BOUND:
+    if workload in MFMA_BOUND:
         gu_flops = 4.0 * H * (P * I + T * Is)
         achieved = gu_flops / (gu_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_BF16, 4),
-                "traffic": read_counters(args.workload)}
+                "traffic": read_counters(workload)}
         layer_frac = {"mfma_frac": round(f_alg / t_layer / PEAK_BF16, 4)}
     else:
         # The gate/up stage on the layer's stream is one streaming launch over
@@ -281,45 +297,29 @@ def main():
         achieved = gu_bytes / (gu_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved * 1e9 / PEAK_HBM, 4),
-                "traffic": read_counters(args.workload)}
+                "traffic": read_counters(workload)}
         layer_frac = {"hbm_frac": round(b_alg / t_layer / PEAK_HBM, 4)}
     roof["kernel"] = "gate_up (grouped gate/up GEMM + SiLU*up)"
-    if args.workload not in MFMA_BOUND and Us != U:
+    if workload not in MFMA_BOUND and Us != U:
         roof["kernel"] += f" streaming launch: {Us} of {U} routed experts + shared"
 
     cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host ...")
-        cpu = cpu_baseline(inp, shape, args.cpu_seconds)
+    if cpu_seconds > 0:
+        log(f"[bench] timing the oracle on the host ({workload}) ...")
+        cpu = cpu_baseline(inp, shape, cpu_seconds)
         log(f"[bench] oracle: {cpu}")
 
-    wl_desc = {"tiny": "tiny parity layer", "decode": "Step-3.5-Flash MoE layer, decode batch",
-               "verify": "Step-3.5-Flash MoE layer, MTP verify batch (64 streams x 4), Zipf experts",
-               "prefill": "Step-3.5-Flash MoE layer, prefill chunk",
-               "int4_decode": "Step-3.5-Flash MoE layer, decode batch, INT4-g32 weights",
-               "mtp_decode": "Step-3.5-Flash last MoE layer (SwiGLU limits 7 / 16), decode batch",
-               "page_router_decode": "Step-3.5-Flash MoE layer under the page's router config "
-                                     "(sigmoid, router bias, x3), decode batch",
-               "step3_decode": "Step-3 MoE layer shape, decode batch",
-               "step3_prefill": "Step-3 MoE layer shape, 4096-token chunk",
-               "dense_decode": "dense SwiGLU FFN (width 11264) as one expert, decode batch",
-               "dense_prefill": "dense SwiGLU FFN (width 11264) as one expert, prefill chunk"}
-    line = {
-        "metric": METRIC,
+    res = {
         "value": round(T / t_layer, 1),
         "unit": "tokens/s",
-        "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if not int4 else "bf16 x int4-g32",
         "data": (f"synthetic (seeded N(0,{shape.x_scale:g}^2) activations, N(0,1/fan_in) weights"
                  + {"zipf": ", Zipf-calibrated router bias", "bias": ", N(0,0.1^2) router bias"}
                  .get(shape.routing, "") + ")"),
-        "config": {"workload": f"{args.workload}: {wl_desc[args.workload]}", "tokens": T,
+        "config": {"workload": f"{workload}: {WL_DESC[workload]}", "tokens": T,
                    "hidden": H, "experts": E, "top_k": k, "expert_inter": I,
                    "shared_inter": Is, "weights": shape.weight_dtype,
                    "routing": shape.routing, "parallelism": "single GPU",
@@ -330,8 +330,6 @@ def main():
                    **({"swiglu_limits": [shape.swiglu_limit, shape.swiglu_limit_shared]}
                       if shape.swiglu_limit or shape.swiglu_limit_shared else {})},
         "roofline": roof,
-        "device": {**device_info(),
-                   "peaks_used": "published: HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s"},
         "layer": {**layer_frac, "alg_bytes": int(b_alg), "alg_flops": int(f_alg),
                   "experts_touched": U,
                   "gate_up_ms_timed": round(gu_ms, 5),
@@ -339,6 +337,48 @@ def main():
                   "stage_ms_note": f"{nb} steps after the timed region, every stage boundary recorded"},
         "cpu_baseline": cpu,
     }
+    del inp, layer, out, ws, route
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is designed, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} bytes 5 times")
+        return
+
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    main_res = measure(args.workload, args, cpu_s)
+    line = {"metric": METRIC, "value": main_res["value"], "unit": main_res["unit"], "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None}
+    for key in ("dtype", "data", "config", "roofline"):
+        line[key] = main_res[key]
+    line["device"] = {**device_info(),
+                      "peaks_used": "published: HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s"}
+    line["layer"] = main_res["layer"]
+    line["cpu_baseline"] = main_res["cpu_baseline"]
+    # The metric's second half: the 16384-token prefill chunk's MFMA fraction,
+    # timed in the same process after the headline workload (same K and W).
+    if args.workload == "decode" and not args.no_prefill:
+        pf = measure("prefill", args, cpu_s)
+        line["prefill"] = {key: pf[key] for key in ("value", "unit", "ms_per_step", "steps",
+                                                    "warmup", "dtype", "config", "roofline",
+                                                    "layer", "cpu_baseline")}
     print(json.dumps(line), flush=True)
 
 
