@@ -41,13 +41,15 @@
  *   - A handle is immutable after moe_layer_create: concurrent forwards on one
  *     handle are allowed when each uses its own workspace and output.
  *   - A handle whose configuration has bf16 weights and activations and
- *     max_tokens >= 256 owns a second stream (default priority, non-blocking),
- *     created with it and destroyed by moe_layer_destroy.  Batches of 256 to
- *     1024 tokens that take the streaming GEMMs put the hot experts' LDS-tiled
- *     GEMMs there (few, long-running workgroups; a load-imbalanced batch has
- *     them): forked from `stream` by an event after the dispatch and joined
- *     back before the combine, so they overlap the streaming GEMMs on
- *     `stream`.  The output is the same as with everything in order.
+ *     max_tokens >= 256 owns a second stream (default priority, non-blocking)
+ *     and two events that fork it from and join it to the caller's stream,
+ *     all created with the handle and destroyed by moe_layer_destroy.
+ *     Batches of 256 to 1024 tokens that take the streaming GEMMs put the hot
+ *     experts' LDS-tiled GEMMs there (few, long-running workgroups; a
+ *     load-imbalanced batch has them): forked from `stream` by an event after
+ *     the dispatch and joined back before the combine, so they overlap the
+ *     streaming GEMMs on `stream`.  The output is the same as with everything
+ *     in order.
  *     Concurrent forwards on one handle share that stream (and serialise
  *     there); while a forward on a handle is being captured into a graph, the
  *     second stream is part of the capture, so no other forward on that handle
@@ -65,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_PACK_VERSION 1
 
 typedef struct moe_layer* moe_layer_t;
@@ -133,7 +135,8 @@ typedef struct {
 
 /* Routing views returned by moe_layer_forward: device pointers into the
  * caller's workspace, valid until the workspace is reused.  Pair p = t*k + j is
- * token t's j-th choice (j in descending-logit order).
+ * token t's j-th choice (j in descending order of selection score; equal
+ * scores in ascending expert order).
  *   topk_idx [T][k] int32, topk_w [T][k] fp32, topk_gap [T] fp32 (k-th minus
  *   (k+1)-th selection score; +inf when k == E);
  *   expert_counts [E] int32; expert_offsets [E+1] int32 (exclusive prefix sum,
@@ -148,16 +151,30 @@ typedef struct {
   int32_t* expert_offsets;
   int32_t* perm;
   int32_t* inv;
+  /* Libraries built with index checks (moe_debug_checks() == 1): two int32,
+   * both 0 unless a kernel of this forward read an out-of-range index (an
+   * expert id in the dispatch, a token id in a GEMM's row gather, a permuted
+   * row in the combine, a tile-list entry); then [0] is its kind (1 expert,
+   * 2 token, 3 row, 4 tile entry) and [1] the first offending value, and the
+   * kernel went on with the index clamped or the tile skipped.  NULL in
+   * release builds. */
+  int32_t* debug_flag;
 } moe_route_t;
 
 /* Version of this header's ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
 
+/* 1 if this library was built with index checks (build option --debug:
+ * moe_route_t.debug_flag), else 0. */
+int moe_debug_checks(void);
+
 /* Validates *cfg, checks that `device` is a gfx950 GPU and returns a handle.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_DEVICE. */
 moe_status_t moe_layer_create(const moe_layer_config_t* cfg, int device, moe_layer_t* out);
 
-/* Releases the handle (host memory only).  NULL is ignored. */
+/* Releases the handle: its host memory and, if it owns them, its second
+ * stream (after that stream's pending work) and the two events that fork and
+ * join it.  NULL is ignored. */
 void moe_layer_destroy(moe_layer_t layer);
 
 /* Bytes of the packed weight buffer (routed experts followed by the shared

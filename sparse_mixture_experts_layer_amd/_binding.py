@@ -1,15 +1,20 @@
 """ctypes declarations of include/moe_layer.h (argument marshalling only).
 
 The shared library is lib/libmoe_mi355x.so inside this package, built by
-`python -m sparse_mixture_experts_layer_amd.build`.  There is no fallback: if
-the library is missing, loading raises.
+`python -m sparse_mixture_experts_layer_amd.build` (with --debug: the
+index-checking build in lib/debug/, which the environment variable
+MOE_MI355X_LIB can name instead).  There is no fallback: if the library is
+missing, loading raises.
 """
 from __future__ import annotations
 
 import ctypes as C
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe_mi355x.so")
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe_mi355x.so")
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "debug",
+                              "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, \
     MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = range(8)
@@ -17,7 +22,7 @@ MOE_F32, MOE_BF16, MOE_INT4_G32 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_STAGE_EVENTS = 6
-MOE_ABI_VERSION = 2     # the header these declarations follow
+MOE_ABI_VERSION = 3     # the header these declarations follow
 STAGES = ("router", "dispatch", "gate_up", "down", "combine")
 
 
@@ -37,7 +42,7 @@ class MoeWeights(C.Structure):
 
 class MoeRoute(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("topk_idx", "topk_w", "topk_gap", "expert_counts",
-                                           "expert_offsets", "perm", "inv")]
+                                           "expert_offsets", "perm", "inv", "debug_flag")]
 
 
 class MoeError(RuntimeError):
@@ -62,6 +67,8 @@ def load() -> C.CDLL:
     lib = C.CDLL(LIB_PATH)
     lib.moe_abi_version.restype = C.c_int
     lib.moe_abi_version.argtypes = []
+    lib.moe_debug_checks.restype = C.c_int
+    lib.moe_debug_checks.argtypes = []
     if lib.moe_abi_version() != MOE_ABI_VERSION:   # struct layouts below would not match
         raise RuntimeError(f"{LIB_PATH} has ABI version {lib.moe_abi_version()}, these bindings "
                            f"expect {MOE_ABI_VERSION} (rebuild: python -m "

@@ -9,6 +9,7 @@
 #include <cfloat>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -48,8 +49,13 @@ struct moe_layer {
   size_t shared_bytes;   // the shared expert, packed
   // second stream (default priority, non-blocking) for the hot experts'
   // LDS-tiled GEMMs, which then overlap the streaming GEMMs; created with the
-  // handle when its configuration can take that path, else null
+  // handle when its configuration can take that path, else null.  The fork
+  // and join events are created with it; aux_mu keeps one forward's fork
+  // record and the second stream's wait on it together (another forward's
+  // record in between would otherwise be the one waited for).
   hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex aux_mu;
 };
 
 namespace {
@@ -93,7 +99,7 @@ moe_status_t check_config(const moe_layer_config_t* c) {
                 c->max_tokens);
   if (c->weight_dtype == MOE_INT4_G32 &&
       (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128))
-    return fail(MOE_ERR_SHAPE, "INT4 weights need hidden, inter and shared_inter % 128 == 0");
+    return fail(MOE_ERR_SHAPE, "INT4 weights need hidden, inter and shared_inter %% 128 == 0");
   return MOE_OK;
 }
 
@@ -108,7 +114,7 @@ struct Plan {
   int ksplit, ksplit_gu;
   size_t gu_part;
   size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, tiles2, ntiles2,
-      done, blk_hist, h, h_lo, h2, y, total;
+      done, dbg, blk_hist, h, h_lo, h2, y, total;
   int large_dispatch;
 };
 
@@ -211,11 +217,15 @@ Plan make_plan(const moe_layer& L, int T) {
   p.tiles2 = take((size_t)p.max_tiles2 * 4);
   p.ntiles2 = take(p.hybrid ? 4 : 0);
   p.done = take(4);
+  p.dbg = take(8);  // debug word pair: code and value of the first out-of-range index
   p.blk_hist = take(p.large_dispatch ? (size_t)moe::dispatch_blocks(T) * E * 4 : 0);
-  // h: fp32 rows on the streaming bf16 path; bf16 in packed fragment order,
-  // with a 16-row gap per group and a tile of slack, on the tiled path
+  // h: rows of hstride on the streaming paths -- fp32 for fp32 activations
+  // with bf16 weights (it enters the down MFMA as hi + lo), bf16 otherwise;
+  // bf16 in packed fragment order, with a 16-row gap per group and a tile of
+  // slack, on the tiled path
   const size_t h_rows_tiled = moe::tiled_h_rows(rows, E);
-  p.h = take(p.tiled ? h_rows_tiled * p.hstride * 2 : (size_t)rows * p.hstride * 4);
+  const size_t h_elem = (c.act_dtype == MOE_F32 && c.weight_dtype == MOE_BF16) ? 4 : 2;
+  p.h = take(p.tiled ? h_rows_tiled * p.hstride * 2 : (size_t)rows * p.hstride * h_elem);
   // bf16 remainder of the shared expert's h: bf16 weights and activations
   const bool lo_plane = p.has_shared && c.weight_dtype == MOE_BF16 && c.act_dtype == MOE_BF16;
   p.h_lo = take(!lo_plane ? 0
@@ -251,8 +261,15 @@ extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+int moe_debug_checks(void) { return MOE_DEBUG ? 1 : 0; }
+
 const char* moe_status_str(moe_status_t s) {
-  switch (s) {
+  // a C caller may pass any int; reading the enum parameter as such a value
+  // would be undefined in C++, so its bytes are read as an int
+  static_assert(sizeof(moe_status_t) == sizeof(int), "moe_status_t is int-sized");
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_NULL: return "MOE_ERR_NULL";
     case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
@@ -291,13 +308,19 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, int device, moe_lay
   L->device = device;
   L->expert_bytes = packed_group_bytes(*cfg, cfg->inter);
   L->shared_bytes = cfg->shared_inter ? packed_group_bytes(*cfg, cfg->shared_inter) : 0;
+  DeviceGuard dg(device);
+  if (dg.err != hipSuccess) {
+    delete L;
+    return fail(MOE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(dg.err));
+  }
   if (cfg->weight_dtype == MOE_BF16 && cfg->act_dtype == MOE_BF16 &&
       cfg->max_tokens >= kHybridMinTokens) {
-    DeviceGuard dg(device);
-    e = dg.err != hipSuccess ? dg.err : hipStreamCreateWithFlags(&L->aux, hipStreamNonBlocking);
+    e = hipStreamCreateWithFlags(&L->aux, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&L->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&L->join, hipEventDisableTiming);
     if (e != hipSuccess) {
-      delete L;
-      return fail(MOE_ERR_DEVICE, "hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+      moe_layer_destroy(L);
+      return fail(MOE_ERR_DEVICE, "second stream or its events: %s", hipGetErrorString(e));
     }
   }
   *out = L;
@@ -306,9 +329,12 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, int device, moe_lay
 
 void moe_layer_destroy(moe_layer_t layer) {
   if (!layer) return;
-  if (layer->aux) {  // its pending work completes before its resources are released
+  if (layer->aux || layer->fork || layer->join) {
+    // the stream's pending work completes before its resources are released
     DeviceGuard dg(layer->device);
-    (void)hipStreamDestroy(layer->aux);
+    if (layer->aux) (void)hipStreamDestroy(layer->aux);
+    if (layer->fork) (void)hipEventDestroy(layer->fork);
+    if (layer->join) (void)hipEventDestroy(layer->join);
   }
   delete layer;
 }
@@ -430,10 +456,11 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   // then ends after the logits); larger batches use the multi-workgroup
   // dispatch after a separate top-k
   int32_t* done = reinterpret_cast<int32_t*>(ws + p.done);
+  int32_t* dbg = reinterpret_cast<int32_t*>(ws + p.dbg);
   hipError_t e = mark(0);
   if (e == hipSuccess)
     e = moe::launch_router_logits(f32, x, static_cast<const uint16_t*>(router_w), part, T, H, E,
-                                  p.ks, p.large_dispatch ? nullptr : done, stream);
+                                  p.ks, p.large_dispatch ? nullptr : done, dbg, stream);
   if (p.large_dispatch) {
     if (e == hipSuccess)
       e = moe::launch_router_topk(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
@@ -442,7 +469,7 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     if (e == hipSuccess)
       e = moe::launch_dispatch_large(idx, T, k, E, p.has_shared, 16 * p.tg,
                                      reinterpret_cast<int32_t*>(ws + p.blk_hist), counts, offsets,
-                                     perm, inv, row_tok, tiles, ntiles, stream);
+                                     perm, inv, row_tok, tiles, ntiles, dbg, stream);
   } else {
     if (e == hipSuccess) e = mark(1);
     const moe::TileLists tl{16 * p.tg, p.hot, 16 * p.tg2, tiles, ntiles,
@@ -451,7 +478,8 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     if (e == hipSuccess)
       e = moe::launch_topk_dispatch(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
                                     c.renormalize, c.routed_scale, idx, wts, gap, done,
-                                    p.has_shared, tl, counts, offsets, perm, inv, row_tok, stream);
+                                    p.has_shared, tl, counts, offsets, perm, inv, row_tok, dbg,
+                                    stream);
   }
   if (e == hipSuccess) e = mark(2);
   moe::GemmGeom g{};
@@ -477,6 +505,7 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g.ksplit_gu = p.ksplit_gu;
   g.gu_part = p.ksplit_gu > 1 ? reinterpret_cast<float*>(ws + p.gu_part) : nullptr;
   g.gu_plane = (size_t)(p.P + (p.has_shared ? T : 0)) * 2 * p.hstride;
+  g.dbg = dbg;
   moe::GemmGeom g2 = g;  // the hybrid's LDS-tiled groups
   g2.tiles = reinterpret_cast<int32_t*>(ws + p.tiles2);
   g2.ntiles = reinterpret_cast<int32_t*>(ws + p.ntiles2);
@@ -500,38 +529,46 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     // workgroups -- go to the handle's second stream, forked after the
     // dispatch and joined before the combine, where they overlap the
     // streaming GEMMs on the caller's stream (they write h2 and their own rows
-    // of Y only).  The events exist for this call only; without them (a failed
-    // creation) the same launches run in order on the caller's stream.
-    hipEvent_t fork = nullptr, join = nullptr;
-    hipStream_t s2 = stream;
-    if (e == hipSuccess && p.hybrid && L->aux &&
-        hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess) {
-      e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventRecord(fork, stream);
-      if (e == hipSuccess) e = hipStreamWaitEvent(L->aux, fork, 0);
-      if (e == hipSuccess) s2 = L->aux;
-    }
+    // of Y only).  The fork record, the second stream's wait on it, the
+    // launches there and the join record are enqueued under the handle's
+    // lock, so a concurrent forward's record cannot come between them; the
+    // caller's stream then waits on the join event (if another forward has
+    // recorded it since, that record is later on the in-order second stream,
+    // so the wait still covers this call's work).
+    const bool fork_join = p.hybrid && L->aux;
+    bool joined = false;  // this call recorded the join event
     if (e == hipSuccess && p.hybrid) {
-      e = moe::launch_gateup_tiled(g2, static_cast<const uint16_t*>(x), row_tok, h2, nullptr,
-                                   p.hstride, s2);
+      std::unique_lock<std::mutex> lk(L->aux_mu, std::defer_lock);
+      hipStream_t s2 = stream;
+      if (fork_join) {
+        lk.lock();
+        e = hipEventRecord(L->fork, stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(L->aux, L->fork, 0);
+        s2 = L->aux;
+      }
+      if (e == hipSuccess)
+        e = moe::launch_gateup_tiled(g2, static_cast<const uint16_t*>(x), row_tok, h2, nullptr,
+                                     p.hstride, s2);
       if (e == hipSuccess) e = moe::launch_down_tiled(g2, h2, nullptr, p.hstride, y, s2);
+      if (fork_join) {  // also after a failed launch: the caller's stream must not run ahead
+        hipError_t r = hipEventRecord(L->join, s2);
+        joined = r == hipSuccess;
+        if (e == hipSuccess) e = r;
+      }
     }
     if (e == hipSuccess)
       e = moe::launch_gateup(g, int4, f32, x, row_tok, h, hl, p.hstride, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = moe::launch_down(g, int4, f32, h, hl, p.hstride, y, stream);
-    if (s2 != stream) {  // also after a failed launch: the caller's stream must not run ahead
-      hipError_t r = hipEventRecord(join, s2);
-      if (r == hipSuccess) r = hipStreamWaitEvent(stream, join, 0);
+    if (joined) {
+      hipError_t r = hipStreamWaitEvent(stream, L->join, 0);
       if (e == hipSuccess) e = r;
     }
-    if (fork) (void)hipEventDestroy(fork);
-    if (join) (void)hipEventDestroy(join);
   }
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
     e = moe::launch_combine(f32, y, H, inv, wts, k, p.P, p.has_shared, out, T, p.ksplit,
-                            g.y_plane, stream);
+                            g.y_plane, dbg, stream);
   if (e == hipSuccess) e = mark(5);
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   if (route) {
@@ -542,6 +579,7 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     route->expert_offsets = offsets;
     route->perm = perm;
     route->inv = inv;
+    route->debug_flag = MOE_DEBUG ? dbg : nullptr;
   }
   return ok();
 }

@@ -22,7 +22,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int k, int P,
                                                       int has_shared, void* __restrict__ out,
-                                                      int T, int planes, size_t plane) {
+                                                      int T, int planes, size_t plane,
+                                                      int32_t* __restrict__ dbg) {
   const int t = blockIdx.x;
   const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
   if (t >= T || col >= H) return;
@@ -32,6 +33,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int j = 0; j < KMAX; ++j) {
     const int jj = j < k ? j : k - 1;
     const int r = inv[(size_t)t * k + jj];
+    dbg_check(dbg, r >= 0 && r < P, kDbgRow, r);
     rows[j] = r < 0 ? 0 : (r >= P ? P - 1 : r);
     wj[j] = w[(size_t)t * k + jj];
   }
@@ -81,13 +83,15 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
                                                            const float* __restrict__ w, int k,
                                                            int P, int has_shared,
                                                            void* __restrict__ out, int T,
-                                                           int planes, size_t plane) {
+                                                           int planes, size_t plane,
+                                                           int32_t* __restrict__ dbg) {
   const int t = blockIdx.x;
   if (t >= T) return;
   __shared__ int rows[kMaxTopK];
   __shared__ float ws[kMaxTopK];
   if (threadIdx.x < k) {
     int r = inv[(size_t)t * k + threadIdx.x];
+    dbg_check(dbg, r >= 0 && r < P, kDbgRow, r);
     rows[threadIdx.x] = r < 0 ? 0 : (r >= P ? P - 1 : r);
     ws[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
   }
@@ -151,22 +155,22 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
 
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
                           int k, int P, int has_shared, void* out, int T, int planes,
-                          size_t plane, hipStream_t s) {
+                          size_t plane, int32_t* dbg, hipStream_t s) {
   if (k < 1 || k > kMaxTopK || planes < 1) return hipErrorInvalidValue;
   if (T >= 512) {  // bandwidth-bound: whole rows per workgroup
     dim3 grid(T), block(256);
     if (out_f32)
       hipLaunchKernelGGL((combine_rows_kernel<true>), grid, block, 0, s, y, H, inv, w, k, P,
-                         has_shared, out, T, planes, plane);
+                         has_shared, out, T, planes, plane, dbg);
     else
       hipLaunchKernelGGL((combine_rows_kernel<false>), grid, block, 0, s, y, H, inv, w, k, P,
-                         has_shared, out, T, planes, plane);
+                         has_shared, out, T, planes, plane, dbg);
     return hipGetLastError();
   }
   dim3 grid(T, (H / 4 + 255) / 256), block(256);
 #define MOE_CB(F32, KM)                                                                          \
   hipLaunchKernelGGL((combine_kernel<F32, KM>), grid, block, 0, s, y, H, inv, w, k, P, has_shared, \
-                     out, T, planes, plane)
+                     out, T, planes, plane, dbg)
 #define MOE_CB_K(F32)                   \
   if (k <= 2) MOE_CB(F32, 2);           \
   else if (k <= 4) MOE_CB(F32, 4);      \

@@ -100,6 +100,26 @@ __device__ __forceinline__ bf16x8 int4_to_bf16x8_biased(uint32_t w) {
   return as_bf16x8(r);
 }
 
+// Index checks of debug builds (compiled with MOE_DEBUG=1).  Where a kernel
+// reads an index from memory and keeps it in range (an expert id, a token id,
+// a permuted row, a tile-list entry), a debug build also reports a value that
+// was out of range: the first report of a call stores its code in flag[0]
+// and the value in flag[1] (a workspace word pair the router kernel clears);
+// the kernel then goes on as a release build does, with the index clamped or
+// the tile skipped -- no trap.  Release builds compile the checks away.
+#ifndef MOE_DEBUG
+#define MOE_DEBUG 0
+#endif
+enum { kDbgExpert = 1, kDbgToken = 2, kDbgRow = 3, kDbgTile = 4 };
+
+__device__ __forceinline__ void dbg_check(int32_t* flag, bool ok, int code, int value) {
+#if MOE_DEBUG
+  if (!ok && flag && atomicCAS(flag, 0, code) == 0) atomicExch(flag + 1, value);
+#else
+  (void)flag, (void)ok, (void)code, (void)value;
+#endif
+}
+
 // Workspace tile-list entry: (group << 16) | m, group = expert (E = shared).
 __device__ __forceinline__ int tile_group(int v) { return v >> 16; }
 __device__ __forceinline__ int tile_m(int v) { return v & 0xffff; }

@@ -62,7 +62,7 @@ template <int NW>
 __device__ __forceinline__ void dispatch_body(
     const int32_t* __restrict__ idx, int T, int k, int E, int has_shared, TileLists lists,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ row_tok) {
+    int32_t* __restrict__ inv, int32_t* __restrict__ row_tok, int32_t* __restrict__ dbg) {
   constexpr int NTH = NW * kWave;
   __shared__ int hist[NW][kMaxExperts];                 // 2 KiB per wave
   __shared__ unsigned long long mask[NW][kMaxExperts];  // 4 KiB per wave
@@ -87,7 +87,10 @@ __device__ __forceinline__ void dispatch_body(
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) ej[j] = idx[(size_t)tl * k + (j < k ? j : k - 1)];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) ej[j] = ej[j] < 0 ? 0 : (ej[j] >= E ? E - 1 : ej[j]);
+  for (int j = 0; j < kMaxTopK; ++j) {
+    dbg_check(dbg, !ok || (ej[j] >= 0 && ej[j] < E), kDbgExpert, ej[j]);
+    ej[j] = ej[j] < 0 ? 0 : (ej[j] >= E ? E - 1 : ej[j]);
+  }
 
   for (int i = tid; i < NW * E; i += NTH) {
     hist[i / E][i % E] = 0;
@@ -197,7 +200,8 @@ __global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
     int E, int k, int score, int renorm, float scale, int32_t* __restrict__ idx,
     float* __restrict__ wout, float* __restrict__ gap, int32_t* __restrict__ done,
     int has_shared, TileLists lists, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_tok) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_tok,
+    int32_t* __restrict__ dbg) {
   __shared__ int last;
   const int t = blockIdx.x * NW + (threadIdx.x >> 6);
   if (t < T) topk_token<NS>(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
   }
   __syncthreads();
   if (!last) return;
-  dispatch_body<NW>(idx, T, k, E, has_shared, lists, counts, offsets, perm, inv, row_tok);
+  dispatch_body<NW>(idx, T, k, E, has_shared, lists, counts, offsets, perm, inv, row_tok, dbg);
 }
 
 // ---------------------------------------------------------------- large batches
@@ -224,7 +228,8 @@ constexpr int kBlkWaves = 4;
 constexpr int kBlkTokens = kBlkWaves * kWave;  // one 64-token step per wave
 
 __global__ __launch_bounds__(kBlkWaves * kWave) void dispatch_hist_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ blk_hist) {
+    const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ blk_hist,
+    int32_t* __restrict__ dbg) {
   __shared__ int hist[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
@@ -232,6 +237,7 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void dispatch_hist_kernel(
   if (t < T)
     for (int j = 0; j < k; ++j) {
       int e = idx[(size_t)t * k + j];
+      dbg_check(dbg, e >= 0 && e < E, kDbgExpert, e);
       e = e < 0 ? 0 : (e >= E ? E - 1 : e);
       atomicAdd(&hist[e], 1);
     }
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(
 __global__ __launch_bounds__(kBlkWaves * kWave) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int has_shared,
     const int32_t* __restrict__ blk_first, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ row_tok) {
+    int32_t* __restrict__ row_tok, int32_t* __restrict__ dbg) {
   __shared__ int base[kBlkWaves][kMaxExperts];
   __shared__ unsigned long long mask[kBlkWaves][kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -322,6 +328,7 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void dispatch_scatter_kernel(
     ej[j] = 0;
     if (j < k && ok) {
       int e = idx[(size_t)t * k + j];
+      dbg_check(dbg, e >= 0 && e < E, kDbgExpert, e);
       ej[j] = e < 0 ? 0 : (e >= E ? E - 1 : e);
       atomicOr(&mask[wave][ej[j]], 1ull << lane);
     }
@@ -358,10 +365,10 @@ int dispatch_blocks(int T) { return (T + kBlkTokens - 1) / kBlkTokens; }
 hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
                                  int32_t* blk_hist, int32_t* counts, int32_t* offsets,
                                  int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* tiles,
-                                 int32_t* ntiles, hipStream_t s) {
+                                 int32_t* ntiles, int32_t* dbg, hipStream_t s) {
   const int nblk = dispatch_blocks(T);
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nblk), dim3(kBlkTokens), 0, s, idx, T, k, E,
-                     blk_hist);
+                     blk_hist, dbg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kDispThreads), 0, s, blk_hist, nblk, T, k,
@@ -369,7 +376,7 @@ hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int ha
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(kBlkTokens), 0, s, idx, T, k, E,
-                     has_shared, blk_hist, perm, inv, row_tok);
+                     has_shared, blk_hist, perm, inv, row_tok, dbg);
   return hipGetLastError();
 }
 
@@ -377,7 +384,8 @@ hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, in
                                 int E, int k, int score, int renorm, float scale, int32_t* idx,
                                 float* w, float* gap, int32_t* done, int has_shared,
                                 const TileLists& tl, int32_t* counts, int32_t* offsets,
-                                int32_t* perm, int32_t* inv, int32_t* row_tok, hipStream_t s) {
+                                int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* dbg,
+                                hipStream_t s) {
   if (T < 1 || T > kDispThreads || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
   if (tl.bm < 1 || (tl.hot > 0 && (tl.bm2 < 1 || !tl.tiles2 || !tl.ntiles2)))
     return hipErrorInvalidValue;
@@ -386,7 +394,7 @@ hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, in
 #define MOE_TD(NW, NS)                                                                          \
   hipLaunchKernelGGL((topk_dispatch_kernel<NW, NS>), dim3((T + NW - 1) / NW), dim3(NW * 64), 0, \
                      s, part, ks, bias, bias_mode, T, E, k, score, renorm, scale, idx, w, gap,    \
-                     done, has_shared, tl, counts, offsets, perm, inv, row_tok)
+                     done, has_shared, tl, counts, offsets, perm, inv, row_tok, dbg)
 #define MOE_TD_NS(NW)                    \
   switch (topk_slots(E)) {               \
     case 1: MOE_TD(NW, 1); break;        \

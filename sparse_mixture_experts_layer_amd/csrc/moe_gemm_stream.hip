@@ -82,6 +82,10 @@ __device__ __forceinline__ bool tile_info(const GemmGeom& g, int tile, TileInfo&
   if (tile >= *g.ntiles) return false;
   const int v = g.tiles[tile];
   ti.group = tile_group(v);
+  if (MOE_DEBUG && (ti.group < 0 || ti.group > g.E)) {  // never written by the dispatch
+    dbg_check(g.dbg, false, kDbgTile, v);
+    return false;
+  }
   const int bm = 16 * g.tg;
   const int m = tile_m(v);
   ti.row0 = g.offsets[ti.group] + m * bm;
@@ -97,12 +101,13 @@ struct TileRows {
   bool ok[TG];
   // gathered activation rows (token ids via row_tok), row stride H
   __device__ __forceinline__ void gather(const TileInfo& ti, const int32_t* row_tok, int T, int H,
-                                         int lane) {
+                                         int lane, int32_t* dbg) {
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
       const int r = t * 16 + (lane & 15);
       ok[t] = r < ti.nrows;
       int tok = ok[t] ? row_tok[ti.row0 + r] : 0;
+      dbg_check(dbg, tok >= 0 && tok < T, kDbgToken, tok);
       tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
       off[t] = (size_t)tok * H + (lane >> 4) * 8;
     }
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
     if (f0 >= ti.width) return;
     K = H;
     wp += (size_t)(f0 / 32) * (K / 32) * kBlockBytes;
-    rows.gather(ti, row_tok, g.T, H, lane);
+    rows.gather(ti, row_tok, g.T, H, lane, g.dbg);
   } else {
     f0 = nb * 256 + wave * 64;
     if (f0 >= H) return;
@@ -305,7 +310,7 @@ void stream_int4_kernel(GemmGeom g, const void* __restrict__ a_src,
     K = H;
     qp = base + (size_t)(f0 / 32) * (K / 128) * kBlockBytes;
     sp = base + (size_t)W * H + (size_t)(f0 / 32) * (K / 128) * 512;
-    rows.gather(ti, row_tok, g.T, H, lane);
+    rows.gather(ti, row_tok, g.T, H, lane, g.dbg);
   } else {
     f0 = nb * 256 + wave * 64;
     if (f0 >= H) return;

@@ -125,6 +125,10 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   if (w >= total) return;
   const int v0 = g.tiles[w / nblk];
   const int group = tile_group(v0);
+  if (MOE_DEBUG && (group < 0 || group > g.E)) {  // never written by the dispatch
+    dbg_check(g.dbg, false, kDbgTile, v0);
+    return;
+  }
   int nb, mt;
   if (MODE == 0 || TM == 256) {  // m-tiles fastest inside the group, in blocks of kMB
     const int first = w / nblk - tile_m(v0);
@@ -187,6 +191,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         int r = 32 * wave + 8 * u + (lane >> 3);
         if (r >= nrows) r = 0;  // any valid row: its C row is never stored
         int tok = row_tok[row0 + r];
+        dbg_check(g.dbg, tok >= 0 && tok < g.T, kDbgToken, tok);
         tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
         const int q = (lane & 7) ^ (lane >> 3);
         a_off[u] = (size_t)tok * H + (size_t)kbeg * 32 + q * 8;
@@ -199,6 +204,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         int r = (2 * wave + f) * 16 + (lane & 15);
         if (r >= nrows) r = 0;  // any valid row: its C row is never stored
         int tok = row_tok[row0 + r];
+        dbg_check(g.dbg, tok >= 0 && tok < g.T, kDbgToken, tok);
         tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
         a_off[f] = (size_t)tok * H + (size_t)kbeg * 32 + (lane >> 4) * 8;
       } else {

@@ -5,14 +5,21 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Index checks of debug builds (see moe_common.hpp); 0 in release builds.
+#ifndef MOE_DEBUG
+#define MOE_DEBUG 0
+#endif
+
 namespace moe {
 
 // ---- router: logits (fp32 partial sums over KS slices of H) + top-k ----------
 // Workgroups of the router logits kernel for a batch (before the K split).
 int router_blocks(bool x_f32, int T, int E);
-// done, if not null, is set to 0 (the counter of launch_topk_dispatch).
+// done, if not null, is set to 0 (the counter of launch_topk_dispatch); so
+// are dbg[0] and dbg[1], if dbg is not null (the debug word pair).
 hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
-                                int T, int H, int E, int ks, int32_t* done, hipStream_t s);
+                                int T, int H, int E, int ks, int32_t* done, int32_t* dbg,
+                                hipStream_t s);
 hipError_t launch_router_topk(const float* part, int ks, const float* bias, int bias_mode, int T,
                               int E, int k, int score, int renorm, float scale, int32_t* idx,
                               float* w, float* gap, hipStream_t s);
@@ -38,7 +45,8 @@ hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, in
                                 int E, int k, int score, int renorm, float scale, int32_t* idx,
                                 float* w, float* gap, int32_t* done, int has_shared,
                                 const TileLists& tl, int32_t* counts, int32_t* offsets,
-                                int32_t* perm, int32_t* inv, int32_t* row_tok, hipStream_t s);
+                                int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* dbg,
+                                hipStream_t s);
 
 // Multi-workgroup variant for large batches (same outputs); blk_hist is
 // scratch of dispatch_blocks(T) * E int32.
@@ -46,7 +54,7 @@ int dispatch_blocks(int T);
 hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
                                  int32_t* blk_hist, int32_t* counts, int32_t* offsets,
                                  int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* tiles,
-                                 int32_t* ntiles, hipStream_t s);
+                                 int32_t* ntiles, int32_t* dbg, hipStream_t s);
 
 // ---- grouped expert GEMMs ----------------------------------------------------
 struct GemmGeom {
@@ -73,6 +81,7 @@ struct GemmGeom {
   int ksplit_gu;
   float* gu_part;
   size_t gu_plane;
+  int32_t* dbg;  // debug word pair (debug builds report out-of-range indices there)
 };
 
 // h[row][f] = silu(x W_gate^T) * (x W_up^T) for every permuted row; h is fp32
@@ -112,7 +121,7 @@ hipError_t launch_gateup_reduce(const GemmGeom& g, int rows, uint16_t* h, uint16
 // then the sum of its planes, added in plane order.
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
                           int k, int P, int has_shared, void* out, int T, int planes,
-                          size_t plane, hipStream_t s);
+                          size_t plane, int32_t* dbg, hipStream_t s);
 
 // ---- weight packing ----------------------------------------------------------
 // bf16 [N][K] of S sources (1 or 2) -> blocks of F*S fragments per 32-k step.

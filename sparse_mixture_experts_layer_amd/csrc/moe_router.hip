@@ -34,10 +34,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
                                                             const uint16_t* __restrict__ wr,
                                                             float* __restrict__ part, int T, int H,
                                                             int E, int kchunk,
-                                                            int32_t* __restrict__ done) {
+                                                            int32_t* __restrict__ done,
+                                                            int32_t* __restrict__ dbg) {
   constexpr int kBatch = 4;
   __shared__ f32x4 red[3][NT][kWave];
-  if (done && blockIdx.x + blockIdx.y + blockIdx.z + threadIdx.x == 0) *done = 0;
+  if (blockIdx.x + blockIdx.y + blockIdx.z + threadIdx.x == 0) {
+    if (done) *done = 0;
+    if (dbg) dbg[0] = dbg[1] = 0;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * 16 * NT;
   const int e0 = blockIdx.y * 16;
@@ -153,9 +157,12 @@ constexpr int kRlStages = 3;
 
 __global__ __launch_bounds__(512, 1) void router_logits_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ part,
-    int T, int H, int E, int kchunk, int32_t* __restrict__ done) {
+    int T, int H, int E, int kchunk, int32_t* __restrict__ done, int32_t* __restrict__ dbg) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kRlStages * kRlStage];
-  if (done && blockIdx.x + blockIdx.y + blockIdx.z + threadIdx.x == 0) *done = 0;
+  if (blockIdx.x + blockIdx.y + blockIdx.z + threadIdx.x == 0) {
+    if (done) *done = 0;
+    if (dbg) dbg[0] = dbg[1] = 0;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wt = wave & 3, we = wave >> 2;
   const int t0 = blockIdx.x * kRlTokens, e0 = blockIdx.y * kRlExperts;
@@ -292,19 +299,20 @@ int router_blocks(bool x_f32, int T, int E) {
 }
 
 hipError_t launch_router_logits(bool x_f32, const void* x, const uint16_t* router_w, float* part,
-                                int T, int H, int E, int ks, int32_t* done, hipStream_t s) {
+                                int T, int H, int E, int ks, int32_t* done, int32_t* dbg,
+                                hipStream_t s) {
   const int kchunk = H / ks;
   const RouterShape r = router_shape(x_f32, T);
   dim3 grid((T + 16 * r.nt - 1) / (16 * r.nt), (E + 16 * r.ne * r.nw - 1) / (16 * r.ne * r.nw), ks);
   if (r.lds) {
     hipLaunchKernelGGL(router_logits_lds_kernel, grid, dim3(512), 0, s,
-                       static_cast<const uint16_t*>(x), router_w, part, T, H, E, kchunk, done);
+                       static_cast<const uint16_t*>(x), router_w, part, T, H, E, kchunk, done, dbg);
     return hipGetLastError();
   }
   dim3 block(256);
 #define MOE_ROUTER_CASE(XF, NT_)                                                              \
   hipLaunchKernelGGL((router_logits_kernel<XF, NT_>), grid, block, 0, s, x, router_w, part, T, H, \
-                     E, kchunk, done)
+                     E, kchunk, done, dbg)
   if (x_f32) {
     if (r.nt == 2) MOE_ROUTER_CASE(true, 2);
     else MOE_ROUTER_CASE(true, 4);

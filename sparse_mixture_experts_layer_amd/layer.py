@@ -53,6 +53,7 @@ class Route:
     expert_offsets: torch.Tensor  # [E+1] int32
     perm: torch.Tensor           # [T*k] int32
     inv: torch.Tensor            # [T*k] int32
+    debug_flag: Optional[torch.Tensor] = None  # [2] int32 (index-checking builds only)
 
 
 class MoELayer:
@@ -225,6 +226,7 @@ class MoELayer:
                      view(r.expert_counts, E, torch.int32),
                      view(r.expert_offsets, E + 1, torch.int32),
                      view(r.perm, T * k, torch.int32),
-                     view(r.inv, T * k, torch.int32))
+                     view(r.inv, T * k, torch.int32),
+                     view(r.debug_flag, 2, torch.int32) if r.debug_flag else None)
 
     __call__ = forward

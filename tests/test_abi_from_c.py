@@ -52,4 +52,4 @@ def test_header_and_library_from_c(tmp_path):
     assert cc.returncode == 0, cc.stderr[-2000:]
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
-    assert run.stdout.strip() == "ok 2"
+    assert run.stdout.strip() == "ok 3"
