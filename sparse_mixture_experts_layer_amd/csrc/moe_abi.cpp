@@ -112,6 +112,10 @@ struct Plan {
   // the LDS-tiled down GEMM's K split (Y then holds ksplit partial-sum planes)
   // and the gate/up's (partial gate/up planes in gu_part, reduced into h)
   int ksplit, ksplit_gu;
+  // LDS-tiled down GEMM without a K split: routed rows of Y in bf16, weighted
+  // by their pair's gate weight (yb = y), the shared rows fp32 (ys)
+  int y_bf16;
+  size_t ys;
   size_t gu_part;
   size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, tiles2, ntiles2,
       done, dbg, blk_hist, h, h_lo, h2, y, total;
@@ -233,7 +237,18 @@ Plan make_plan(const moe_layer& L, int T) {
                           : (size_t)T * p.hstride * 2);
   // the hybrid's LDS-tiled groups (routed only): packed h of their own
   p.h2 = take(p.hybrid ? h_rows_tiled * p.hstride * 2 : 0);
-  p.y = take((size_t)p.ksplit * rows * c.hidden * 4);
+  // Y: fp32 rows (ksplit partial-sum planes of them for a split K), or, for
+  // the LDS-tiled GEMMs without a split, the routed rows as bf16 of w * Y --
+  // half the bytes the down GEMM writes and the combine reads at prefill; the
+  // rounding of w * Y is about 1/8 of a rounding of Y -- and the shared
+  // expert's rows, which enter unweighted, in fp32
+  p.y_bf16 = p.tiled && p.ksplit == 1;
+  if (p.y_bf16) {
+    p.y = take((size_t)p.P * c.hidden * 2);
+    p.ys = take(p.has_shared ? (size_t)T * c.hidden * 4 : 0);
+  } else {
+    p.y = take((size_t)p.ksplit * rows * c.hidden * 4);
+  }
   p.gu_part = take(p.ksplit_gu > 1 ? (size_t)p.ksplit_gu * rows * 2 * p.hstride * 4 : 0);
   p.total = o;
   return p;
@@ -506,12 +521,18 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g.gu_part = p.ksplit_gu > 1 ? reinterpret_cast<float*>(ws + p.gu_part) : nullptr;
   g.gu_plane = (size_t)(p.P + (p.has_shared ? T : 0)) * 2 * p.hstride;
   g.dbg = dbg;
+  g.y_bf16 = p.y_bf16;
+  g.yb = p.y_bf16 ? reinterpret_cast<uint16_t*>(ws + p.y) : nullptr;
+  g.ys = p.y_bf16 && p.has_shared ? reinterpret_cast<float*>(ws + p.ys) : nullptr;
+  g.pair_w = wts;
+  g.perm = perm;
   moe::GemmGeom g2 = g;  // the hybrid's LDS-tiled groups
   g2.tiles = reinterpret_cast<int32_t*>(ws + p.tiles2);
   g2.ntiles = reinterpret_cast<int32_t*>(ws + p.ntiles2);
   g2.max_tiles = p.max_tiles2;
   g2.tg = p.tg2;
   g2.shared_tiles = 0;
+  g2.y_bf16 = 0;  // beside the streaming GEMMs, which write fp32 Y rows
   if (p.tiled) {
     uint16_t* hb = reinterpret_cast<uint16_t*>(h);
     uint16_t* hl = reinterpret_cast<uint16_t*>(ws + p.h_lo);
@@ -568,7 +589,7 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
     e = moe::launch_combine(f32, y, H, inv, wts, k, p.P, p.has_shared, out, T, p.ksplit,
-                            g.y_plane, dbg, stream);
+                            g.y_plane, g.yb, g.ys, dbg, stream);
   if (e == hipSuccess) e = mark(5);
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   if (route) {

@@ -10,6 +10,19 @@
 namespace moe {
 namespace {
 
+// Four output columns at element offset off, rounded once to the output dtype.
+template <bool OUT_F32>
+__device__ __forceinline__ void store_out(void* out, size_t off, const f32x4& acc) {
+  if (OUT_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = acc;
+  } else {
+    uint2 pk;
+    pk.x = pack_bf16x2(acc[0], acc[1]);
+    pk.y = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + off) = pk;
+  }
+}
+
 // Small batches: one thread per 4 output columns of one token, a token's
 // row spread over ceil(H / 1024) workgroups.  The token's routing entries are
 // the same for every thread (scalar loads), and the thread issues the loads of
@@ -17,12 +30,14 @@ namespace {
 // for each row in turn): rows past k re-read row k-1 and are zeroed by a
 // select.  Y is read once: nontemporal loads keep it from displacing cached
 // data.
-template <bool OUT_F32, int KMAX>
+template <bool OUT_F32, int KMAX, bool YB>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int H,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int k, int P,
                                                       int has_shared, void* __restrict__ out,
                                                       int T, int planes, size_t plane,
+                                                      const uint16_t* __restrict__ yb,
+                                                      const float* __restrict__ ys,
                                                       int32_t* __restrict__ dbg) {
   const int t = blockIdx.x;
   const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
@@ -38,6 +53,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     wj[j] = w[(size_t)t * k + jj];
   }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  if (YB) {  // routed rows already weighted, in bf16; the shared row in fp32
+    u32x2 b[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      b[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(yb + (size_t)rows[j] * H + col));
+    f32x4 acc = has_shared ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ys + (size_t)t * H + col))
+                           : zero;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) break;
+      acc[0] += bf16_bits_to_f32((uint16_t)b[j][0]);
+      acc[1] += bf16_bits_to_f32((uint16_t)(b[j][0] >> 16));
+      acc[2] += bf16_bits_to_f32((uint16_t)b[j][1]);
+      acc[3] += bf16_bits_to_f32((uint16_t)(b[j][1] >> 16));
+    }
+    store_out<OUT_F32>(out, (size_t)t * H + col, acc);
+    return;
+  }
   // shared row (or, without a shared expert, any valid row, then zeroed)
   const size_t srow = has_shared ? (size_t)(P + t) : (size_t)rows[0];
   f32x4 sh = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + srow * H + col));
@@ -64,26 +97,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += cw * vj[e];
   }
-  if (OUT_F32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)t * H + col) = acc;
-  } else {
-    uint2 pk;
-    pk.x = pack_bf16x2(acc[0], acc[1]);
-    pk.y = pack_bf16x2(acc[2], acc[3]);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * H + col) = pk;
-  }
+  store_out<OUT_F32>(out, (size_t)t * H + col, acc);
 }
 
 // Large batches: one workgroup per token, a thread owns 4 groups of 4
 // columns; the rows are walked in order, the 4 groups' loads of a row in
 // flight together, so each row is read as one contiguous run per workgroup.
-template <bool OUT_F32>
+template <bool OUT_F32, bool YB>
 __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ y, int H,
                                                            const int32_t* __restrict__ inv,
                                                            const float* __restrict__ w, int k,
                                                            int P, int has_shared,
                                                            void* __restrict__ out, int T,
                                                            int planes, size_t plane,
+                                                           const uint16_t* __restrict__ yb,
+                                                           const float* __restrict__ ys,
                                                            int32_t* __restrict__ dbg) {
   const int t = blockIdx.x;
   if (t >= T) return;
@@ -101,6 +129,38 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
   // Y is read once: nontemporal loads keep it from displacing cached data.
   constexpr int kChunks = 4;
   const int stride = blockDim.x * 4;
+  if (YB) {  // routed rows already weighted, in bf16; the shared row in fp32
+    for (int c0 = 0; c0 < H; c0 += stride * kChunks) {
+      f32x4 acc[kChunks];
+      int col[kChunks];
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        col[i] = c0 + i * stride + threadIdx.x * 4;
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (has_shared && col[i] < H)
+          acc[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ys + (size_t)t * H + col[i]));
+      }
+      for (int j = 0; j < k; ++j) {
+        const uint16_t* yr = yb + (size_t)rows[j] * H;
+        u32x2 v[kChunks];
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i)
+          v[i] = col[i] < H ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(yr + col[i]))
+                            : u32x2{0u, 0u};
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+          acc[i][0] += bf16_bits_to_f32((uint16_t)v[i][0]);
+          acc[i][1] += bf16_bits_to_f32((uint16_t)(v[i][0] >> 16));
+          acc[i][2] += bf16_bits_to_f32((uint16_t)v[i][1]);
+          acc[i][3] += bf16_bits_to_f32((uint16_t)(v[i][1] >> 16));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i)
+        if (col[i] < H) store_out<OUT_F32>(out, (size_t)t * H + col[i], acc[i]);
+    }
+    return;
+  }
   for (int c0 = 0; c0 < H; c0 += stride * kChunks) {
     f32x4 acc[kChunks];
     int col[kChunks];
@@ -137,17 +197,8 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
         for (int e = 0; e < 4; ++e) acc[i][e] += wj * v[i][e];
     }
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      if (col[i] >= H) continue;
-      if (OUT_F32) {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)t * H + col[i]) = acc[i];
-      } else {
-        uint2 pk;
-        pk.x = pack_bf16x2(acc[i][0], acc[i][1]);
-        pk.y = pack_bf16x2(acc[i][2], acc[i][3]);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * H + col[i]) = pk;
-      }
-    }
+    for (int i = 0; i < kChunks; ++i)
+      if (col[i] < H) store_out<OUT_F32>(out, (size_t)t * H + col[i], acc[i]);
   }
 }
 
@@ -155,22 +206,34 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
 
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
                           int k, int P, int has_shared, void* out, int T, int planes,
-                          size_t plane, int32_t* dbg, hipStream_t s) {
-  if (k < 1 || k > kMaxTopK || planes < 1) return hipErrorInvalidValue;
+                          size_t plane, const uint16_t* yb, const float* ys, int32_t* dbg,
+                          hipStream_t s) {
+  if (k < 1 || k > kMaxTopK || planes < 1 || (yb && (planes != 1 || (has_shared && !ys))))
+    return hipErrorInvalidValue;
+  const bool ybm = yb != nullptr;
   if (T >= 512) {  // bandwidth-bound: whole rows per workgroup
     dim3 grid(T), block(256);
-    if (out_f32)
-      hipLaunchKernelGGL((combine_rows_kernel<true>), grid, block, 0, s, y, H, inv, w, k, P,
-                         has_shared, out, T, planes, plane, dbg);
-    else
-      hipLaunchKernelGGL((combine_rows_kernel<false>), grid, block, 0, s, y, H, inv, w, k, P,
-                         has_shared, out, T, planes, plane, dbg);
+#define MOE_CR(F32, YB)                                                                          \
+  hipLaunchKernelGGL((combine_rows_kernel<F32, YB>), grid, block, 0, s, y, H, inv, w, k, P,     \
+                     has_shared, out, T, planes, plane, yb, ys, dbg)
+    if (out_f32) {
+      if (ybm) MOE_CR(true, true); else MOE_CR(true, false);
+    } else {
+      if (ybm) MOE_CR(false, true); else MOE_CR(false, false);
+    }
+#undef MOE_CR
     return hipGetLastError();
   }
   dim3 grid(T, (H / 4 + 255) / 256), block(256);
 #define MOE_CB(F32, KM)                                                                          \
-  hipLaunchKernelGGL((combine_kernel<F32, KM>), grid, block, 0, s, y, H, inv, w, k, P, has_shared, \
-                     out, T, planes, plane, dbg)
+  do {                                                                                           \
+    if (ybm)                                                                                     \
+      hipLaunchKernelGGL((combine_kernel<F32, KM, true>), grid, block, 0, s, y, H, inv, w, k, P, \
+                         has_shared, out, T, planes, plane, yb, ys, dbg);                        \
+    else                                                                                         \
+      hipLaunchKernelGGL((combine_kernel<F32, KM, false>), grid, block, 0, s, y, H, inv, w, k,   \
+                         P, has_shared, out, T, planes, plane, yb, ys, dbg);                     \
+  } while (0)
 #define MOE_CB_K(F32)                   \
   if (k <= 2) MOE_CB(F32, 2);           \
   else if (k <= 4) MOE_CB(F32, 4);      \

@@ -82,6 +82,15 @@ struct GemmGeom {
   float* gu_part;
   size_t gu_plane;
   int32_t* dbg;  // debug word pair (debug builds report out-of-range indices there)
+  // LDS-tiled down GEMM without a K split, y_bf16 set: a routed row of Y is
+  // stored as bf16 of its pair's gate weight times the row (yb, [P][H], row =
+  // permuted row), the shared group's rows as fp32 (ys, [T][H], row = token);
+  // pair_w[perm[row]] is a routed row's weight.
+  int y_bf16;
+  uint16_t* yb;
+  float* ys;
+  const float* pair_w;
+  const int32_t* perm;
 };
 
 // h[row][f] = silu(x W_gate^T) * (x W_up^T) for every permuted row; h is fp32
@@ -118,10 +127,13 @@ hipError_t launch_gateup_reduce(const GemmGeom& g, int rows, uint16_t* h, uint16
 
 // ---- combine: out[t] = Y[shared row of t] + sum_j w[t,j] Y[inv[t,j]] -------
 // Y may come in `planes` partial-sum planes, `plane` floats apart: each row is
-// then the sum of its planes, added in plane order.
+// then the sum of its planes, added in plane order.  With yb (the LDS-tiled
+// down GEMM's y_bf16 layout), the routed rows come from yb, already weighted
+// (out[t] = ys[t] + sum_j yb[inv[t,j]]), the shared ones from ys.
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
                           int k, int P, int has_shared, void* out, int T, int planes,
-                          size_t plane, int32_t* dbg, hipStream_t s);
+                          size_t plane, const uint16_t* yb, const float* ys, int32_t* dbg,
+                          hipStream_t s);
 
 // ---- weight packing ----------------------------------------------------------
 // bf16 [N][K] of S sources (1 or 2) -> blocks of F*S fragments per 32-k step.
