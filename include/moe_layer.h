@@ -25,8 +25,9 @@
  *     N rows of K elements, the nn.Linear [out][in] order).
  *   - Device pointers must be 16-byte aligned.  The caller owns every device
  *     buffer (activations, router weights, packed weights, output, workspace);
- *     the library allocates no device memory.  A handle owns host state (and
- *     for some configurations one HIP stream, below).
+ *     the library allocates no device memory, apart from the static scratch
+ *     array of moe_layer_forward_noalloc (one per GPU, below).  A handle owns
+ *     host state (and for some configurations one HIP stream, below).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream),
  *     which must belong to the handle's device (the call makes that device
  *     current while it enqueues and restores the caller's afterwards).
@@ -206,6 +207,31 @@ moe_status_t moe_layer_forward(moe_layer_t layer, int32_t num_tokens, const void
                                const void* router_w, const float* router_bias,
                                const void* packed, void* out, void* workspace,
                                size_t workspace_bytes, moe_route_t* route, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_layer_forward without a workspace argument.  Its scratch is one static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one copy per
+ * GPU, taken when the first handle on that GPU is created and held until the
+ * process ends; the call itself allocates nothing and runs the same kernels
+ * as moe_layer_forward (same results bit for bit).
+ *   - num_tokens must need at most MOE_NOALLOC_SCRATCH_BYTES of workspace
+ *     (moe_layer_workspace_bytes); a larger batch returns MOE_ERR_WORKSPACE
+ *     before anything is enqueued.  64 MiB holds a 256-token batch of the
+ *     Step-3.5-Flash layer (H 4096, 288 experts, top-8, widths 1280).
+ *   - Every call on one GPU shares that GPU's array: calls whose work
+ *     overlaps on the device (other streams, other handles, other threads)
+ *     race and give undefined results.  Serialise them (one stream, or events).
+ *   - route views point into that array and stay valid until the next call
+ *     on the same GPU.  Nothing in it needs to be zero at the start of a call
+ *     (the one counter the kernels use is cleared by a kernel of the call).
+ *   - Errors: those of moe_layer_forward, MOE_ERR_WORKSPACE as above, and
+ *     MOE_ERR_DEVICE if the array's device address could not be taken. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_layer_forward_noalloc(moe_layer_t layer, int32_t num_tokens, const void* x,
+                                       const void* router_w, const float* router_bias,
+                                       const void* packed, void* out, moe_route_t* route,
+                                       hipStream_t stream);
 
 /* Number of events moe_layer_forward_timed records. */
 #define MOE_STAGE_EVENTS 6

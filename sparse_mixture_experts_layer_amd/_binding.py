@@ -22,6 +22,7 @@ MOE_F32, MOE_BF16, MOE_INT4_G32 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_STAGE_EVENTS = 6
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # scratch of moe_layer_forward_noalloc, per GPU
 MOE_ABI_VERSION = 3     # the header these declarations follow
 STAGES = ("router", "dispatch", "gate_up", "down", "combine")
 
@@ -90,6 +91,10 @@ def load() -> C.CDLL:
                                       C.POINTER(MoeRoute), C.c_void_p]
     lib.moe_layer_forward_timed.restype = C.c_int
     lib.moe_layer_forward_timed.argtypes = lib.moe_layer_forward.argtypes + [C.c_void_p]
+    lib.moe_layer_forward_noalloc.restype = C.c_int
+    lib.moe_layer_forward_noalloc.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                              C.c_void_p, C.c_void_p, C.c_void_p,
+                                              C.POINTER(MoeRoute), C.c_void_p]
     lib.moe_status_str.restype = C.c_char_p
     lib.moe_status_str.argtypes = [C.c_int]
     lib.moe_last_error.restype = C.c_char_p
@@ -109,6 +114,23 @@ def last_error() -> str:
 def check(status: int, where: str) -> None:
     if status != MOE_OK:
         raise MoeError(status, where, last_error())
+
+
+_hip = None
+
+
+def memcpy_d2d_async(dst: int, src: int, nbytes: int, stream: int) -> None:
+    """hipMemcpyAsync device to device on `stream`, through the HIP runtime the
+    process already loaded (torch's)."""
+    global _hip
+    if _hip is None:
+        h = C.CDLL("libamdhip64.so.7")
+        h.hipMemcpyAsync.restype = C.c_int
+        h.hipMemcpyAsync.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
+        _hip = h
+    HIP_MEMCPY_DEVICE_TO_DEVICE = 3
+    if _hip.hipMemcpyAsync(dst, src, nbytes, HIP_MEMCPY_DEVICE_TO_DEVICE, stream) != 0:
+        raise RuntimeError("hipMemcpyAsync failed")
 
 
 # hip_runtime_api.h: an event that skips the system-scope fence of its record

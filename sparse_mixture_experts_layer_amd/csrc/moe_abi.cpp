@@ -270,6 +270,41 @@ struct DeviceGuard {
   }
 };
 
+// ---- scratch of the allocation-free entry point -----------------------------
+// One static device array per GPU the library runs on (the code object's
+// copy on that device), held until the process ends.  In host code `scratch`
+// only stands in for the symbol: its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device while that device is current
+// (moe_layer_create, the library's set-up call) and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The calling thread's current device must be `device`.
+void scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[device]) return;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  g_scratch_err[device] = e;
+  if (e == hipSuccess) g_scratch[device] = ptr;
+  else (void)hipGetLastError();  // a later launch check must not report this failure
+}
+
+void* scratch_of(int device, hipError_t* err) {
+  if (device < 0 || device >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  *err = g_scratch_err[device];
+  return g_scratch[device];
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,6 +373,7 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, int device, moe_lay
       return fail(MOE_ERR_DEVICE, "second stream or its events: %s", hipGetErrorString(e));
     }
   }
+  scratch_setup(device);
   *out = L;
   return ok();
 }
@@ -615,6 +651,28 @@ moe_status_t moe_layer_forward(moe_layer_t L, int32_t T, const void* x, const vo
                                hipStream_t stream) {
   return forward_impl(L, T, x, router_w, router_bias, packed, out, workspace, workspace_bytes,
                       route, stream, nullptr);
+}
+
+moe_status_t moe_layer_forward_noalloc(moe_layer_t L, int32_t T, const void* x,
+                                       const void* router_w, const float* router_bias,
+                                       const void* packed, void* out, moe_route_t* route,
+                                       hipStream_t stream) {
+  if (!L) return fail(MOE_ERR_NULL, "layer is NULL");
+  if (T > 0 && T <= L->cfg.max_tokens) {
+    const size_t need = make_plan(*L, T).total;
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE_ERR_WORKSPACE,
+                  "num_tokens %d needs %zu bytes of scratch; the allocation-free entry point has "
+                  "%zu per device (call moe_layer_forward with a workspace instead)",
+                  T, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  }
+  hipError_t err = hipSuccess;
+  void* ws = scratch_of(L->device, &err);
+  if (!ws)
+    return fail(MOE_ERR_DEVICE, "no scratch address for device %d: %s", L->device,
+                hipGetErrorString(err));
+  return forward_impl(L, T, x, router_w, router_bias, packed, out, ws,
+                      MOE_NOALLOC_SCRATCH_BYTES, route, stream, nullptr);
 }
 
 moe_status_t moe_layer_forward_timed(moe_layer_t L, int32_t T, const void* x,

@@ -211,6 +211,53 @@ class MoELayer:
             return out
         return out, self._route_views(route, workspace, T)
 
+    def forward_noalloc(self, x: torch.Tensor, router_w: torch.Tensor,
+                        router_bias: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, packed: Optional[torch.Tensor] = None,
+                        return_route: bool = False):
+        """y = layer(x) through moe_layer_forward_noalloc: the library's static
+        per-GPU scratch replaces the workspace (calls that overlap on one GPU
+        race).  With return_route, the routing results are copied out of that
+        scratch into new tensors on the current stream."""
+        c = self.cfg
+        T = x.shape[0]
+        dev = self.device
+        _need(x, "x", self.act_dtype, (T, c.hidden), dev)
+        _need(router_w, "router_w", torch.bfloat16, (c.num_experts, c.hidden), dev)
+        if router_bias is not None:
+            _need(router_bias, "router_bias", torch.float32, (c.num_experts,), dev)
+        packed = self.packed if packed is None else packed
+        if packed is None:
+            raise RuntimeError("weights are not packed (call pack first)")
+        _need_bytes(packed, "packed", self.packed_bytes, dev)
+        if out is None:
+            out = torch.empty((T, c.hidden), dtype=self.act_dtype, device=dev)
+        else:
+            _need(out, "out", self.act_dtype, (T, c.hidden), dev)
+        route = B.MoeRoute()
+        B.check(self.lib.moe_layer_forward_noalloc(
+            self._h, T, x.data_ptr(), router_w.data_ptr(), _ptr(router_bias), packed.data_ptr(),
+            out.data_ptr(), C.byref(route), self._stream()), "moe_layer_forward_noalloc")
+        if not return_route:
+            return out
+        k, E = c.top_k, c.num_experts
+
+        def copy(ptr, shape, dtype):
+            t = torch.empty(shape, dtype=dtype, device=dev)
+            if t.numel():
+                B.memcpy_d2d_async(t.data_ptr(), ptr, t.numel() * t.element_size(),
+                                   self._stream())
+            return t
+
+        return out, Route(copy(route.topk_idx, (T, k), torch.int32),
+                          copy(route.topk_w, (T, k), torch.float32),
+                          copy(route.topk_gap, (T,), torch.float32),
+                          copy(route.expert_counts, (E,), torch.int32),
+                          copy(route.expert_offsets, (E + 1,), torch.int32),
+                          copy(route.perm, (T * k,), torch.int32),
+                          copy(route.inv, (T * k,), torch.int32),
+                          copy(route.debug_flag, (2,), torch.int32) if route.debug_flag else None)
+
     def _route_views(self, r: "B.MoeRoute", ws: torch.Tensor, T: int) -> Route:
         c = self.cfg
         base = ws.data_ptr()

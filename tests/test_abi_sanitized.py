@@ -82,6 +82,7 @@ int main(void) {
   EXPECT(moe_layer_pack_weights(NULL, NULL, NULL, NULL) == MOE_ERR_NULL, 44);
   moe_route_t r;
   EXPECT(moe_layer_forward(NULL, 4, NULL, NULL, NULL, NULL, NULL, NULL, 0, &r, NULL) == MOE_ERR_NULL, 45);
+  EXPECT(moe_layer_forward_noalloc(NULL, 4, NULL, NULL, NULL, NULL, NULL, &r, NULL) == MOE_ERR_NULL, 46);
   EXPECT(moe_layer_forward_timed(NULL, 4, NULL, NULL, NULL, NULL, NULL, NULL, 0, &r, NULL, NULL) == MOE_ERR_NULL, 47);
   EXPECT(moe_debug_checks() == 0, 48);
   printf("ok\n");
