@@ -165,7 +165,7 @@ def cpu_baseline(inp, shape, target_s: float):
     info = threadpoolctl.threadpool_info()
     cores = max([d.get("num_threads", 1) for d in info] or [1])
     T = x64.shape[0]
-    s, elapsed = 1, 0.0
+    s, elapsed, spent = 1, 0.0, 0.0
     while True:
         idx, *_ = oracle.route(x64[:s], wr, bias, shape.top_k, shape.score, shape.renormalize,
                                shape.routed_scale, shape.bias_mode)
@@ -176,7 +176,10 @@ def cpu_baseline(inp, shape, target_s: float):
                        shape.renormalize, shape.routed_scale, shape.bias_mode,
                        swiglu_limit=shape.swiglu_limit, swiglu_limit_shared=shape.swiglu_limit_shared)
         elapsed = time.perf_counter() - t0
-        if elapsed >= target_s or s >= T:
+        spent += elapsed
+        log(f"[bench]   oracle on {s} tokens: {elapsed:.1f} s")
+        # stop at about target_s per run, and after about 3 x target_s in all
+        if elapsed >= target_s or s >= T or spent + 2.2 * elapsed > 3 * target_s:
             break
         s = min(T, s * 2 if elapsed < target_s / 4 else max(s + 1, int(s * target_s / elapsed)))
         host.clear()
