@@ -112,10 +112,11 @@ struct Plan {
   // the LDS-tiled down GEMM's K split (Y then holds ksplit partial-sum planes)
   // and the gate/up's (partial gate/up planes in gu_part, reduced into h)
   int ksplit, ksplit_gu;
-  // LDS-tiled down GEMM without a K split: routed rows of Y in bf16, weighted
-  // by their pair's gate weight (yb = y), the shared rows fp32 (ys)
+  // bf16 activations and no K split: the down GEMMs weight the routed rows of
+  // Y by their gate weights (row_w, written by the dispatch) and store them in
+  // bf16 at the pairs' rows (yb = y), the shared rows in fp32 (ys)
   int y_bf16;
-  size_t ys;
+  size_t ys, row_w;
   size_t gu_part;
   size_t part, idx, w, gap, counts, offsets, perm, inv, row_tok, tiles, ntiles, tiles2, ntiles2,
       done, dbg, blk_hist, h, h_lo, h2, y, total;
@@ -237,12 +238,14 @@ Plan make_plan(const moe_layer& L, int T) {
                           : (size_t)T * p.hstride * 2);
   // the hybrid's LDS-tiled groups (routed only): packed h of their own
   p.h2 = take(p.hybrid ? h_rows_tiled * p.hstride * 2 : 0);
-  // Y: fp32 rows (ksplit partial-sum planes of them for a split K), or, for
-  // the LDS-tiled GEMMs without a split, the routed rows as bf16 of w * Y --
-  // half the bytes the down GEMM writes and the combine reads at prefill; the
-  // rounding of w * Y is about 1/8 of a rounding of Y -- and the shared
-  // expert's rows, which enter unweighted, in fp32
-  p.y_bf16 = p.tiled && p.ksplit == 1;
+  // Y: fp32 rows (ksplit partial-sum planes of them for a split K), or, with
+  // bf16 activations and no split, the routed rows as bf16 of w * Y at the
+  // pairs' rows -- half the bytes the down GEMM writes and the combine reads,
+  // whose loads then need no index; the rounding of w * Y is about 1/8 of a
+  // rounding of Y -- and the shared expert's rows, which enter unweighted, in
+  // fp32
+  p.y_bf16 = c.act_dtype == MOE_BF16 && p.ksplit == 1;
+  p.row_w = take(p.y_bf16 ? (size_t)p.P * 4 : 0);
   if (p.y_bf16) {
     p.y = take((size_t)p.P * c.hidden * 2);
     p.ys = take(p.has_shared ? (size_t)T * c.hidden * 4 : 0);
@@ -495,6 +498,7 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   int32_t* ntiles = reinterpret_cast<int32_t*>(ws + p.ntiles);
   float* h = reinterpret_cast<float*>(ws + p.h);
   float* y = reinterpret_cast<float*>(ws + p.y);
+  float* row_w = p.y_bf16 ? reinterpret_cast<float*>(ws + p.row_w) : nullptr;
   const bool f32 = c.act_dtype == MOE_F32;
   const bool int4 = c.weight_dtype == MOE_INT4_G32;
   const int E = c.num_experts, H = c.hidden, k = c.top_k;
@@ -520,7 +524,7 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     if (e == hipSuccess)
       e = moe::launch_dispatch_large(idx, T, k, E, p.has_shared, 16 * p.tg,
                                      reinterpret_cast<int32_t*>(ws + p.blk_hist), counts, offsets,
-                                     perm, inv, row_tok, tiles, ntiles, dbg, stream);
+                                     perm, inv, row_tok, tiles, ntiles, wts, row_w, dbg, stream);
   } else {
     if (e == hipSuccess) e = mark(1);
     const moe::TileLists tl{16 * p.tg, p.hot, 16 * p.tg2, tiles, ntiles,
@@ -529,8 +533,8 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
     if (e == hipSuccess)
       e = moe::launch_topk_dispatch(part, p.ks, router_bias, c.bias_mode, T, E, k, c.score,
                                     c.renormalize, c.routed_scale, idx, wts, gap, done,
-                                    p.has_shared, tl, counts, offsets, perm, inv, row_tok, dbg,
-                                    stream);
+                                    p.has_shared, tl, counts, offsets, perm, inv, row_tok, row_w,
+                                    dbg, stream);
   }
   if (e == hipSuccess) e = mark(2);
   moe::GemmGeom g{};
@@ -560,7 +564,7 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g.y_bf16 = p.y_bf16;
   g.yb = p.y_bf16 ? reinterpret_cast<uint16_t*>(ws + p.y) : nullptr;
   g.ys = p.y_bf16 && p.has_shared ? reinterpret_cast<float*>(ws + p.ys) : nullptr;
-  g.pair_w = wts;
+  g.row_w = row_w;
   g.perm = perm;
   moe::GemmGeom g2 = g;  // the hybrid's LDS-tiled groups
   g2.tiles = reinterpret_cast<int32_t*>(ws + p.tiles2);
@@ -568,7 +572,6 @@ moe_status_t forward_impl(moe_layer_t L, int32_t T, const void* x, const void* r
   g2.max_tiles = p.max_tiles2;
   g2.tg = p.tg2;
   g2.shared_tiles = 0;
-  g2.y_bf16 = 0;  // beside the streaming GEMMs, which write fp32 Y rows
   if (p.tiled) {
     uint16_t* hb = reinterpret_cast<uint16_t*>(h);
     uint16_t* hl = reinterpret_cast<uint16_t*>(ws + p.h_lo);

@@ -1,6 +1,9 @@
 // Combine / unpermute: y[t] = Y[shared row of t] + sum_j w[t,j] * Y[inv[t,j]],
 // accumulated in fp32 in a fixed order (shared first, then j = 0..k-1) and
-// rounded once to the output dtype.  The shared expert is always on and enters
+// rounded once to the output dtype.  Down GEMMs that weight their rows
+// themselves (bf16 activations, no K split) leave bf16 rows of w[t,j] * Y at
+// the pairs' rows t*k + j and the shared rows in fp32 by token: then
+// y[t] = ys[t] + sum_j yb[t*k + j], in the same order.  The shared expert is always on and enters
 // unweighted (llm-atlas "Step-3.5-Flash", "Champs bruts du config.json",
 // share_expert_dim; that it is added outside the renormalised weights is the
 // reading taken where the pages are silent).
@@ -42,22 +45,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = blockIdx.x;
   const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
   if (t >= T || col >= H) return;
-  int rows[KMAX];
-  float wj[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    const int jj = j < k ? j : k - 1;
-    const int r = inv[(size_t)t * k + jj];
-    dbg_check(dbg, r >= 0 && r < P, kDbgRow, r);
-    rows[j] = r < 0 ? 0 : (r >= P ? P - 1 : r);
-    wj[j] = w[(size_t)t * k + jj];
-  }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  if (YB) {  // routed rows already weighted, in bf16; the shared row in fp32
+  if (YB) {  // routed rows already weighted, in bf16, at the pairs' rows; the shared row in fp32
     u32x2 b[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      b[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(yb + (size_t)rows[j] * H + col));
+      b[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2*>(yb + ((size_t)t * k + (j < k ? j : k - 1)) * H + col));
     f32x4 acc = has_shared ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ys + (size_t)t * H + col))
                            : zero;
 #pragma unroll
@@ -70,6 +64,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     store_out<OUT_F32>(out, (size_t)t * H + col, acc);
     return;
+  }
+  int rows[KMAX];
+  float wj[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int jj = j < k ? j : k - 1;
+    const int r = inv[(size_t)t * k + jj];
+    dbg_check(dbg, r >= 0 && r < P, kDbgRow, r);
+    rows[j] = r < 0 ? 0 : (r >= P ? P - 1 : r);
+    wj[j] = w[(size_t)t * k + jj];
   }
   // shared row (or, without a shared expert, any valid row, then zeroed)
   const size_t srow = has_shared ? (size_t)(P + t) : (size_t)rows[0];
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
   if (t >= T) return;
   __shared__ int rows[kMaxTopK];
   __shared__ float ws[kMaxTopK];
-  if (threadIdx.x < k) {
+  if (!YB && threadIdx.x < k) {  // (bf16 rows: the pairs' own rows, already weighted)
     int r = inv[(size_t)t * k + threadIdx.x];
     dbg_check(dbg, r >= 0 && r < P, kDbgRow, r);
     rows[threadIdx.x] = r < 0 ? 0 : (r >= P ? P - 1 : r);
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
           acc[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ys + (size_t)t * H + col[i]));
       }
       for (int j = 0; j < k; ++j) {
-        const uint16_t* yr = yb + (size_t)rows[j] * H;
+        const uint16_t* yr = yb + ((size_t)t * k + j) * H;
         u32x2 v[kChunks];
 #pragma unroll
         for (int i = 0; i < kChunks; ++i)

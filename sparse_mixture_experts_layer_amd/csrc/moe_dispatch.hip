@@ -62,7 +62,8 @@ template <int NW>
 __device__ __forceinline__ void dispatch_body(
     const int32_t* __restrict__ idx, int T, int k, int E, int has_shared, TileLists lists,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ row_tok, int32_t* __restrict__ dbg) {
+    int32_t* __restrict__ inv, int32_t* __restrict__ row_tok, const float* __restrict__ w,
+    float* __restrict__ row_w, int32_t* __restrict__ dbg) {
   constexpr int NTH = NW * kWave;
   __shared__ int hist[NW][kMaxExperts];                 // 2 KiB per wave
   __shared__ unsigned long long mask[NW][kMaxExperts];  // 4 KiB per wave
@@ -84,8 +85,12 @@ __device__ __forceinline__ void dispatch_body(
   const bool ok = lane < tw && t < tend;
   const int tl = ok ? t : 0;
   int ej[kMaxTopK];
+  float wj[kMaxTopK];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) ej[j] = idx[(size_t)tl * k + (j < k ? j : k - 1)];
+  for (int j = 0; j < kMaxTopK; ++j) {
+    ej[j] = idx[(size_t)tl * k + (j < k ? j : k - 1)];
+    wj[j] = row_w ? w[(size_t)tl * k + (j < k ? j : k - 1)] : 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     dbg_check(dbg, !ok || (ej[j] >= 0 && ej[j] < E), kDbgExpert, ej[j]);
@@ -179,6 +184,7 @@ __device__ __forceinline__ void dispatch_body(
         perm[row] = p;
         inv[p] = row;
         row_tok[row] = t;
+        if (row_w) row_w[row] = wj[j];
       }
     }
   }
@@ -187,9 +193,124 @@ __device__ __forceinline__ void dispatch_body(
     for (int t = tid; t < T; t += NTH) row_tok[P + t] = t;
 }
 
+// Up to 64 tokens, the dispatch by one wave, lane = token: per expert, a
+// 64-bit LDS mask of the tokens that chose it (a token holds an expert once),
+// its popcount the expert's count; lane l scans the counts (and tile counts)
+// of experts l*per .. l*per+per-1 with a wave-wide prefix sum; a pair's row
+// is its expert's first row plus the tokens below it in that expert's mask.
+// Same outputs as dispatch_body, which keeps the batches with a second tile
+// list (never this small).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void dispatch_wave(const int32_t* __restrict__ idx, int T, int k, int E,
+                                              int has_shared, const TileLists& lists,
+                                              int32_t* __restrict__ counts,
+                                              int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                              int32_t* __restrict__ row_tok,
+                                              const float* __restrict__ w,
+                                              float* __restrict__ row_w,
+                                              int32_t* __restrict__ dbg) {
+  __shared__ unsigned long long mask[kMaxExperts];
+  __shared__ int first[kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int P = T * k;
+  const bool ok = lane < T;
+  // this lane's token's choices (a lane without a token re-reads token 0;
+  // choices past k re-read the last one), in flight while the masks clear
+  int ej[kMaxTopK];
+  float wj[kMaxTopK];
+  {
+    const int tl = ok ? lane : 0;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      ej[j] = idx[(size_t)tl * k + (j < k ? j : k - 1)];
+      wj[j] = row_w ? w[(size_t)tl * k + (j < k ? j : k - 1)] : 0.f;
+    }
+  }
+  for (int e = lane; e < E; e += kWave) mask[e] = 0ull;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    dbg_check(dbg, !ok || (ej[j] >= 0 && ej[j] < E), kDbgExpert, ej[j]);
+    ej[j] = ej[j] < 0 ? 0 : (ej[j] >= E ? E - 1 : ej[j]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (ok) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k)
+        __hip_atomic_fetch_or(&mask[ej[j]], 1ull << lane, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WAVEFRONT);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // counts, rows and tiles of experts e0 .. e0+per-1
+  const int per = (E + kWave - 1) / kWave, e0 = lane * per;
+  int c[kMaxExperts / kWave], sum = 0, nts = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxExperts / kWave; ++i) {
+    const int e = e0 + i;
+    c[i] = (i < per && e < E) ? __popcll(mask[e]) : 0;
+    sum += c[i];
+    nts += (c[i] + lists.bm - 1) / lists.bm;
+  }
+  const int incl = wave_incl_scan(sum), incl_t = wave_incl_scan(nts);
+  int row = incl - sum, tile = incl_t - nts;
+#pragma unroll
+  for (int i = 0; i < kMaxExperts / kWave; ++i) {
+    const int e = e0 + i;
+    if (i < per && e < E) {
+      counts[e] = c[i];
+      offsets[e] = row;
+      first[e] = row;
+      const int nt = (c[i] + lists.bm - 1) / lists.bm;
+      for (int m = 0; m < nt; ++m) lists.tiles[tile + m] = (e << 16) | m;
+      row += c[i];
+      tile += nt;
+    }
+  }
+  const int routed_tiles = __shfl(incl_t, kWave - 1);
+  const int shared_tiles = has_shared ? (T + lists.bm - 1) / lists.bm : 0;
+  for (int m = lane; m < shared_tiles; m += kWave) lists.tiles[routed_tiles + m] = (E << 16) | m;
+  if (lane == 0) {
+    counts[E] = has_shared ? T : 0;
+    offsets[E] = P;
+    offsets[E + 1] = P + (has_shared ? T : 0);
+    lists.ntiles[0] = routed_tiles + shared_tiles;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // stable scatter
+  if (ok) {
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        const int r = first[ej[j]] + __popcll(mask[ej[j]] & below);
+        const int p = lane * k + j;
+        perm[r] = p;
+        inv[p] = r;
+        row_tok[r] = lane;
+        if (row_w) row_w[r] = wj[j];
+      }
+    }
+    if (has_shared) row_tok[P + lane] = lane;
+  }
+}
+
 // Top-k for NW tokens per workgroup (one wave each), then the workgroup that
-// finishes last runs the dispatch: one launch less on the path of small
-// batches.  `done` counts finished workgroups; the router logits kernel
+// finishes last runs the dispatch (one wave of it up to 64 tokens): one
+// launch less on the path of small batches.  `done` counts finished
+// workgroups; the router logits kernel
 // clears it earlier on the same stream.  After the workgroup barrier (its
 // waves' choices are in this XCD's L2), one thread releases them device-wide
 // and counts the workgroup; the thread that counts last acquires every
@@ -201,7 +322,7 @@ __global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
     float* __restrict__ wout, float* __restrict__ gap, int32_t* __restrict__ done,
     int has_shared, TileLists lists, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_tok,
-    int32_t* __restrict__ dbg) {
+    float* __restrict__ row_w, int32_t* __restrict__ dbg) {
   __shared__ int last;
   const int t = blockIdx.x * NW + (threadIdx.x >> 6);
   if (t < T) topk_token<NS>(part, ks, bias, bias_mode, T, E, k, score, renorm, scale, t, idx, wout, gap);
@@ -215,7 +336,16 @@ __global__ __launch_bounds__(NW * 64) void topk_dispatch_kernel(
   }
   __syncthreads();
   if (!last) return;
-  dispatch_body<NW>(idx, T, k, E, has_shared, lists, counts, offsets, perm, inv, row_tok, dbg);
+  if constexpr (NW == 4) {  // the launch shape of up to 256 tokens
+    if (T <= kWave && lists.hot == 0) {
+      if (threadIdx.x < kWave)
+        dispatch_wave(idx, T, k, E, has_shared, lists, counts, offsets, perm, inv, row_tok, wout,
+                      row_w, dbg);
+      return;
+    }
+  }
+  dispatch_body<NW>(idx, T, k, E, has_shared, lists, counts, offsets, perm, inv, row_tok, wout,
+                    row_w, dbg);
 }
 
 // ---------------------------------------------------------------- large batches
@@ -310,7 +440,8 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(
 __global__ __launch_bounds__(kBlkWaves * kWave) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int has_shared,
     const int32_t* __restrict__ blk_first, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ row_tok, int32_t* __restrict__ dbg) {
+    int32_t* __restrict__ row_tok, const float* __restrict__ w, float* __restrict__ row_w,
+    int32_t* __restrict__ dbg) {
   __shared__ int base[kBlkWaves][kMaxExperts];
   __shared__ unsigned long long mask[kBlkWaves][kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -353,6 +484,7 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void dispatch_scatter_kernel(
       perm[row] = p;
       inv[p] = row;
       row_tok[row] = t;
+      if (row_w) row_w[row] = w[p];
     }
   }
   if (has_shared && ok) row_tok[P + t] = t;
@@ -365,7 +497,8 @@ int dispatch_blocks(int T) { return (T + kBlkTokens - 1) / kBlkTokens; }
 hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
                                  int32_t* blk_hist, int32_t* counts, int32_t* offsets,
                                  int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* tiles,
-                                 int32_t* ntiles, int32_t* dbg, hipStream_t s) {
+                                 int32_t* ntiles, const float* w, float* row_w, int32_t* dbg,
+                                 hipStream_t s) {
   const int nblk = dispatch_blocks(T);
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nblk), dim3(kBlkTokens), 0, s, idx, T, k, E,
                      blk_hist, dbg);
@@ -376,7 +509,7 @@ hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int ha
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(kBlkTokens), 0, s, idx, T, k, E,
-                     has_shared, blk_hist, perm, inv, row_tok, dbg);
+                     has_shared, blk_hist, perm, inv, row_tok, w, row_w, dbg);
   return hipGetLastError();
 }
 
@@ -384,8 +517,8 @@ hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, in
                                 int E, int k, int score, int renorm, float scale, int32_t* idx,
                                 float* w, float* gap, int32_t* done, int has_shared,
                                 const TileLists& tl, int32_t* counts, int32_t* offsets,
-                                int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* dbg,
-                                hipStream_t s) {
+                                int32_t* perm, int32_t* inv, int32_t* row_tok, float* row_w,
+                                int32_t* dbg, hipStream_t s) {
   if (T < 1 || T > kDispThreads || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
   if (tl.bm < 1 || (tl.hot > 0 && (tl.bm2 < 1 || !tl.tiles2 || !tl.ntiles2)))
     return hipErrorInvalidValue;
@@ -394,7 +527,7 @@ hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, in
 #define MOE_TD(NW, NS)                                                                          \
   hipLaunchKernelGGL((topk_dispatch_kernel<NW, NS>), dim3((T + NW - 1) / NW), dim3(NW * 64), 0, \
                      s, part, ks, bias, bias_mode, T, E, k, score, renorm, scale, idx, w, gap,    \
-                     done, has_shared, tl, counts, offsets, perm, inv, row_tok, dbg)
+                     done, has_shared, tl, counts, offsets, perm, inv, row_tok, row_w, dbg)
 #define MOE_TD_NS(NW)                    \
   switch (topk_slots(E)) {               \
     case 1: MOE_TD(NW, 1); break;        \

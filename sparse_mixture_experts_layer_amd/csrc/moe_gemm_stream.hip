@@ -123,6 +123,134 @@ struct TileRows {
   }
 };
 
+// ---------------------------------------------------------- down GEMM output
+// With g.y_bf16 a routed row goes to yb at its pair's row, as bf16 of its gate
+// weight times the row, and a shared-expert row to ys at its token's row in
+// fp32; both are staged through LDS (a private region per wave, rows padded
+// against bank conflicts) so that each lane stores 16 contiguous bytes -- from
+// the MFMA layout a lane would store 4 bytes at a time and a wave 64-byte
+// pieces, a long tail at the end of every workgroup.  Ordinary stores: with
+// the nontemporal hint the INT4 decode layer measured 1.6% slower.  Otherwise fp32 rows of
+// Y at the permuted row, stored from the MFMA layout.
+// The rows' gate weights (staging layout: row t*16 + 4*(lane/16) + i) and
+// pairs (store layout: row 8q + lane/8), loaded before the first weight loads
+// and copied to a per-wave LDS region once those are issued, so that no
+// register stays live across the k loop (the INT4 kernel has none to spare):
+// the copy waits for these loads only, which land with the first weight
+// blocks the loop waits for anyway.  Rows past the tile read its first row.
+template <int TG>
+struct DownRows {
+  static constexpr int kSlots = 6 * TG;  // 4*TG weights, then 2*TG pairs, 64 lanes each
+  uint32_t v[kSlots];
+  __device__ __forceinline__ void fetch(const GemmGeom& g, const TileInfo& ti, int lane) {
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = t * 16 + (lane >> 4) * 4 + i;
+        v[t * 4 + i] = __float_as_uint(g.row_w[ti.row0 + (r < ti.nrows ? r : 0)]);
+      }
+#pragma unroll
+    for (int q = 0; q < 2 * TG; ++q) {
+      const int r = q * 8 + (lane >> 3);
+      v[4 * TG + q] = (uint32_t)g.perm[ti.row0 + (r < ti.nrows ? r : 0)];
+    }
+  }
+  __device__ __forceinline__ void stash(uint32_t* region, int lane) const {
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) region[j * kWave + lane] = v[j];
+  }
+};
+
+// Per-wave LDS of the down epilogue: row weights and pairs, then the staging
+// rows (pitch 68 floats for fp32, 72 halves for bf16, against bank conflicts).
+template <int TG>
+struct DownLds {
+  static constexpr int kPF = 68, kPB = 72;
+  uint32_t rows[4][DownRows<TG>::kSlots * kWave];
+  float stg[4][16 * TG * kPF];
+};
+
+// The kernel's DownLds, allocated only in the kernels that can store bf16 Y
+// (bf16 activations), null in the others.
+template <int TG, bool USE>
+__device__ __forceinline__ DownLds<TG>* down_lds() {
+  if constexpr (USE) {
+    __shared__ DownLds<TG> d;
+    return &d;
+  } else {
+    return nullptr;
+  }
+}
+
+template <int TG>
+__device__ __forceinline__ void store_down(const GemmGeom& g, const TileInfo& ti,
+                                           const f32x4 (&acc)[TG][4], DownLds<TG>* sh, int f0,
+                                           float* __restrict__ out, int wave, int lane) {
+  const int H = g.H;
+  if (!g.y_bf16 || !sh) {
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = t * 16 + (lane >> 4) * 4 + i;
+        if (r >= ti.nrows) continue;
+        const size_t row = (size_t)ti.row0 + r;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) out[row * H + f0 + f * 16 + (lane & 15)] = acc[t][f][i];
+      }
+    return;
+  }
+  constexpr int kPF = DownLds<TG>::kPF, kPB = DownLds<TG>::kPB;
+  float* st = sh->stg[wave];
+  if (ti.group == g.E) {
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          st[(t * 16 + (lane >> 4) * 4 + i) * kPF + f * 16 + (lane & 15)] = acc[t][f][i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int tok0 = ti.row0 - g.offsets[g.E];
+#pragma unroll
+    for (int q = 0; q < 4 * TG; ++q) {
+      const int r = q * 4 + (lane >> 4);
+      if (r < ti.nrows) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(st + r * kPF + (lane & 15) * 4);
+        *reinterpret_cast<f32x4*>(g.ys + (size_t)(tok0 + r) * H + f0 + (lane & 15) * 4) = v;
+      }
+    }
+    return;
+  }
+  const uint32_t* rw = sh->rows[wave];
+  uint16_t* sb = reinterpret_cast<uint16_t*>(st);
+#pragma unroll
+  for (int t = 0; t < TG; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float wr = __uint_as_float(rw[(t * 4 + i) * kWave + lane]);
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        sb[(t * 16 + (lane >> 4) * 4 + i) * kPB + f * 16 + (lane & 15)] =
+            f32_to_bf16_bits(wr * acc[t][f][i]);
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int q = 0; q < 2 * TG; ++q) {
+    const int r = q * 8 + (lane >> 3);
+    if (r < ti.nrows) {
+      const int p = (int)rw[(4 * TG + q) * kWave + lane];
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * kPB + (lane & 7) * 8);
+      *reinterpret_cast<u32x4*>(g.yb + (size_t)p * H + f0 + (lane & 7) * 8) = v;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ bf16 weights
 // MODE 0: gate/up (A = gathered x, fp32 or bf16; out h with SiLU*up)
 // MODE 1: down    (A = h; out Y fp32)
@@ -185,6 +313,10 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
     for (int t = 0; t < TG; ++t) lo_off[t] = rows.off[t] - (size_t)g.offsets[g.E] * hstride;
   }
   constexpr int NL = LO ? 1 : 0;
+  DownLds<TG>* dsh = down_lds<TG, MODE == 1 && HM != 0>();
+  const bool yrows = dsh && g.y_bf16 && ti.group != g.E;  // workgroup-uniform
+  DownRows<TG> dr;
+  if (yrows) dr.fetch(g, ti, lane);
   u32x4 w[U][4], wn[U][4];
   ARow<AF32> a[U][TG], an[U][TG];
   ARow<false> l[U][TG * NL + 1 - NL], ln[U][TG * NL + 1 - NL];
@@ -198,6 +330,7 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
       if (lo) l[u][t].load(h_lo, lo_off[t] + u * 32, rows.ok[t]);
     }
   }
+  if (yrows) dr.stash(dsh->rows[wave], lane);
   for (int k0 = 0; k0 < nk; k0 += U) {
     const bool more = k0 + U < nk;
     if (more) {
@@ -243,6 +376,10 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
   }
 
   // epilogue: lane holds rows t*16 + 4*(lane/16) + i of weight column (lane % 16)
+  if (MODE == 1) {
+    store_down<TG>(g, ti, acc, dsh, f0, out, wave, lane);
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < TG; ++t)
 #pragma unroll
@@ -269,9 +406,6 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(GemmGeom g, const void
             h_lo[(row - g.offsets[g.E]) * hstride + f0 + f * 16 + (lane & 15)] =
                 f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
         }
-      } else {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) out[row * H + f0 + f * 16 + (lane & 15)] = acc[t][f][i];
       }
     }
 }
@@ -393,8 +527,13 @@ void stream_int4_kernel(GemmGeom g, const void* __restrict__ a_src,
         }
       }
   };
+  DownLds<TG>* dsh = down_lds<TG, MODE == 1>();
+  const bool yrows = dsh && g.y_bf16 && ti.group != g.E;  // workgroup-uniform
+  DownRows<TG> dr;
+  if (yrows) dr.fetch(g, ti, lane);
   load_blk(b0, 0);
   load_blk(b1, 1);
+  if (yrows) dr.stash(dsh->rows[wave], lane);
   int kb = 0;
   for (; kb + 3 <= nkb; kb += 3) {
     load_blk(b2, kb + 2);
@@ -410,6 +549,10 @@ void stream_int4_kernel(GemmGeom g, const void* __restrict__ a_src,
   // 0-2 blocks left, already in b0 (and b1)
   if (kb < nkb) compute(b0);
   if (kb + 1 < nkb) compute(b1);
+  if (MODE == 1) {
+    store_down<TG>(g, ti, acc, dsh, f0, out, wave, lane);
+    return;
+  }
 
 #pragma unroll
   for (int t = 0; t < TG; ++t)
@@ -425,9 +568,6 @@ void stream_int4_kernel(GemmGeom g, const void* __restrict__ a_src,
         for (int f = 0; f < 2; ++f)
           hb[row * hstride + f0 + f * 16 + (lane & 15)] =
               f32_to_bf16_bits(swiglu(acc[t][f][i], acc[t][2 + f][i], lim));
-      } else {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) out[row * H + f0 + f * 16 + (lane & 15)] = acc[t][f][i];
       }
     }
 }

@@ -188,6 +188,17 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   const bool shared = group == g.E;
   const float lim = shared ? g.limit_shared : g.limit;
   const int npass = (MODE == 1 && shared) ? 2 : 1;
+  // routed rows of the down GEMM with y_bf16: lane l holds the gate weight and
+  // the pair of the wave's row wm*64 + l, loaded now for the epilogue
+  const bool yb = MODE == 1 && g.y_bf16 && !shared;
+  float wrow = 0.f;
+  int prow = 0;
+  if (yb) {
+    const int r = wm * 64 + lane;
+    const int rc = row0 + (r < nrows ? r : 0);
+    wrow = g.row_w[rc];
+    prow = g.perm[rc];
+  }
   size_t a_off[4];  // XL: one row per line load; otherwise the first two
   auto set_rows = [&](int pass) {
     if (XL) {
@@ -384,14 +395,8 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     constexpr int kMP = TS::kMP, kPitch = TS::kPitch;
     uint8_t* stg = lds + wave * (kMP * 16 * kPitch);
     const int blk0 = nb * 4 + wn * 2;
-    // bf16 rows weighted by their pair's gate weight (routed groups, no K
-    // split): lane l holds the weight of the wave's row l
-    const bool yb = g.y_bf16 && !shared;
-    float wrow = 0.f;
-    if (yb) {
-      const int r = wm * 64 + lane;
-      wrow = r < nrows ? g.pair_w[g.perm[row0 + r]] : 0.f;
-    }
+    // bf16 rows weighted by their gate weight at their pair's row (routed
+    // groups, no K split)
 #pragma unroll
     for (int pass = 0; pass < 4 / kMP; ++pass) {
 #pragma unroll
@@ -411,20 +416,18 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         const int r = wm * 64 + pass * kMP * 16 + lr;
         const int blk = blk0 + (ch >> 4);
         const float wr = __shfl(wrow, r - wm * 64);
+        const int pr = __shfl(prow, r - wm * 64);
         const size_t col = (size_t)blk * 64 + (ch & 15) * 4;
-        if (r < nrows && blk < nblocks) {  // read once, by combine: nontemporal
+        if (r < nrows && blk < nblocks) {  // ordinary stores: 0.8% ahead of nontemporal ones
           if (yb) {
             const u32x2 pk = {pack_bf16x2(wr * val[0], wr * val[1]),
                               pack_bf16x2(wr * val[2], wr * val[3])};
-            __builtin_nontemporal_store(
-                pk, reinterpret_cast<u32x2*>(g.yb + (size_t)(row0 + r) * H + col));
+            *reinterpret_cast<u32x2*>(g.yb + (size_t)pr * H + col) = pk;
           } else if (g.y_bf16) {  // the shared group: fp32 rows by token
-            __builtin_nontemporal_store(
-                val, reinterpret_cast<f32x4*>(g.ys + (size_t)(row0 + r - g.offsets[g.E]) * H + col));
+            *reinterpret_cast<f32x4*>(g.ys + (size_t)(row0 + r - g.offsets[g.E]) * H + col) = val;
           } else {
-            __builtin_nontemporal_store(
-                val, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + split * g.y_plane +
-                                              (size_t)(row0 + r) * H + col));
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + split * g.y_plane +
+                                      (size_t)(row0 + r) * H + col) = val;
           }
         }
       }

@@ -26,6 +26,8 @@ hipError_t launch_router_topk(const float* part, int ks, const float* bias, int 
 
 // ---- dispatch: counts, offsets, stable permutation, GEMM tile list ----------
 // counts/offsets have E+1 / E+2 entries (group E = shared expert, T rows).
+// row_w, if not null, receives each routed row's gate weight (w of the pair
+// stored at that row), read by the down GEMMs that weight Y themselves.
 // GEMM tile lists written by the dispatch: a routed expert with fewer than
 // `hot` rows goes to list 1 in tiles of bm rows, one with `hot` rows or more
 // to list 2 in tiles of bm2 rows; the shared expert (group E) always to list
@@ -39,14 +41,14 @@ struct TileLists {
 
 // Top-k (as launch_router_topk) and the dispatch in one launch, T <= 1024:
 // the last workgroup to finish its tokens' top-k runs the dispatch as one
-// workgroup.  done is a device counter that must read 0 at launch
+// workgroup (one wave of it up to 64 tokens).  done is a device counter that must read 0 at launch
 // (launch_router_logits clears it).
 hipError_t launch_topk_dispatch(const float* part, int ks, const float* bias, int bias_mode, int T,
                                 int E, int k, int score, int renorm, float scale, int32_t* idx,
                                 float* w, float* gap, int32_t* done, int has_shared,
                                 const TileLists& tl, int32_t* counts, int32_t* offsets,
-                                int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* dbg,
-                                hipStream_t s);
+                                int32_t* perm, int32_t* inv, int32_t* row_tok, float* row_w,
+                                int32_t* dbg, hipStream_t s);
 
 // Multi-workgroup variant for large batches (same outputs); blk_hist is
 // scratch of dispatch_blocks(T) * E int32.
@@ -54,7 +56,8 @@ int dispatch_blocks(int T);
 hipError_t launch_dispatch_large(const int32_t* idx, int T, int k, int E, int has_shared, int bm,
                                  int32_t* blk_hist, int32_t* counts, int32_t* offsets,
                                  int32_t* perm, int32_t* inv, int32_t* row_tok, int32_t* tiles,
-                                 int32_t* ntiles, int32_t* dbg, hipStream_t s);
+                                 int32_t* ntiles, const float* w, float* row_w, int32_t* dbg,
+                                 hipStream_t s);
 
 // ---- grouped expert GEMMs ----------------------------------------------------
 struct GemmGeom {
@@ -82,14 +85,15 @@ struct GemmGeom {
   float* gu_part;
   size_t gu_plane;
   int32_t* dbg;  // debug word pair (debug builds report out-of-range indices there)
-  // LDS-tiled down GEMM without a K split, y_bf16 set: a routed row of Y is
-  // stored as bf16 of its pair's gate weight times the row (yb, [P][H], row =
-  // permuted row), the shared group's rows as fp32 (ys, [T][H], row = token);
-  // pair_w[perm[row]] is a routed row's weight.
+  // y_bf16 set (bf16 activations, no K split): the down GEMMs store a routed
+  // row of Y as bf16 of its gate weight times the row at its pair's row of yb
+  // ([P][H], row p = t*k + j for permuted row r with perm[r] = p), the shared
+  // group's rows as fp32 by token (ys, [T][H]); row_w[r] is routed row r's
+  // gate weight (written by the dispatch).
   int y_bf16;
   uint16_t* yb;
   float* ys;
-  const float* pair_w;
+  const float* row_w;
   const int32_t* perm;
 };
 
@@ -127,9 +131,9 @@ hipError_t launch_gateup_reduce(const GemmGeom& g, int rows, uint16_t* h, uint16
 
 // ---- combine: out[t] = Y[shared row of t] + sum_j w[t,j] Y[inv[t,j]] -------
 // Y may come in `planes` partial-sum planes, `plane` floats apart: each row is
-// then the sum of its planes, added in plane order.  With yb (the LDS-tiled
-// down GEMM's y_bf16 layout), the routed rows come from yb, already weighted
-// (out[t] = ys[t] + sum_j yb[inv[t,j]]), the shared ones from ys.
+// then the sum of its planes, added in plane order.  With yb (the down GEMMs'
+// y_bf16 layout), the routed rows come from yb, already weighted, at the
+// pairs' rows (out[t] = ys[t] + sum_j yb[t*k + j]), the shared ones from ys.
 hipError_t launch_combine(bool out_f32, const float* y, int H, const int32_t* inv, const float* w,
                           int k, int P, int has_shared, void* out, int T, int planes,
                           size_t plane, const uint16_t* yb, const float* ys, int32_t* dbg,

@@ -14,17 +14,17 @@
 
 namespace moe {
 
-// Orderable key of (score, expert): larger key = larger score, and on equal
-// scores the lower expert index.  NaN ranks as -inf.
-__device__ __forceinline__ unsigned long long rank_key(float s, int e) {
+// Orderable 32-bit key of a score: larger key = larger score, NaN ranks as
+// -inf, and every score's key is above 0 (the key of a retired or missing
+// slot).  Equal scores are told apart by the expert index, which the key does
+// not hold: the selection below resolves them.
+__device__ __forceinline__ uint32_t score_key(float s) {
   if (s != s) s = -INFINITY;
-  uint32_t u = __float_as_uint(s);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float key_score(unsigned long long key) {
-  uint32_t u = (uint32_t)(key >> 32);
+__device__ __forceinline__ float key_score(uint32_t u) {
   u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
   return __uint_as_float(u);
 }
@@ -52,34 +52,12 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, F op) {
   return op(h[0], h[1]);
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  auto take = [&](uint32_t lo2, uint32_t hi2) {
-    const unsigned long long o = ((unsigned long long)hi2 << 32) | lo2;
-    const unsigned long long c = ((unsigned long long)hi << 32) | lo;
-    const unsigned long long m = o > c ? o : c;
-    lo = (uint32_t)m;
-    hi = (uint32_t)(m >> 32);
-  };
-  take(dpp<0xB1>(lo), dpp<0xB1>(hi));
-  take(dpp<0x4E>(lo), dpp<0x4E>(hi));
-  take(dpp<0x141>(lo), dpp<0x141>(hi));
-  take(dpp<0x140>(lo), dpp<0x140>(hi));
-  {
-    auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    lo = rl[0];
-    hi = rh[0];
-    take(rl[1], rh[1]);
-  }
-  {
-    auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    lo = rl[0];
-    hi = rh[0];
-    take(rl[1], rh[1]);
-  }
-  return ((unsigned long long)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -103,9 +81,13 @@ inline int topk_slots(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : (E <= 320 ? 
 // One wave selects for token t.  Expert e lives in lane e % 64, slot e / 64
 // (NS slots per lane, NS * 64 >= E).
 // The logits are the sum of the ks K-slice partials part[s][t][e], added in
-// slice order.  Each round takes the wave-wide largest remaining key; the
-// owner lane retires it.  Writes idx[t][j], wout[t][j] (j in descending
-// order) and gap[t].
+// slice order.  Each round takes the wave-wide largest remaining score key
+// (one 32-bit reduction); the lanes holding it are told apart by a ballot --
+// one lane almost always, else the lowest expert index wins through a second
+// reduction -- and the owner lane retires that slot.  Lane r keeps round r's
+// expert and logit, so the k exponentials run side by side after the rounds
+// (their sum still taken in round order).  Writes idx[t][j], wout[t][j] (j in
+// descending order) and gap[t].
 template <int NS>
 __device__ __forceinline__ void topk_token(const float* __restrict__ part, int ks,
                                            const float* __restrict__ bias, int bias_mode, int T,
@@ -114,10 +96,12 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
                                            float* __restrict__ gap) {
   const int lane = threadIdx.x & 63;
   float lg[NS], v[NS];
-  unsigned long long key[NS];
+  uint32_t key[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) v[i] = 0.f;
-  // K-slice partial sums, added in slice order; 8 slices of loads in flight
+  // K-slice partial sums, added in slice order; 8 slices of loads in flight,
+  // each unconditional in the lane (slots past E re-read expert E-1; their
+  // sums are never used)
   for (int s0 = 0; s0 < ks; s0 += 8) {
     float ld[8][NS];
 #pragma unroll
@@ -125,7 +109,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int e = lane + i * kWave;
-        ld[u][i] = (s0 + u < ks && e < E) ? part[((size_t)(s0 + u) * T + t) * E + e] : 0.f;
+        ld[u][i] = s0 + u < ks ? part[((size_t)(s0 + u) * T + t) * E + (e < E ? e : E - 1)] : 0.f;
       }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -143,41 +127,49 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
       bv[i] = bias[e < E ? e : E - 1];
     }
   }
+  const bool select_bias = bias && bias_mode == 1;  // selection score = logit + bias
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int e = lane + i * kWave;
     lg[i] = -INFINITY;
-    key[i] = 0ull;  // below every real key
+    key[i] = 0u;  // below every real key
     if (e < E) {
       const float b = bv[i];
       const float l = (bias && bias_mode == 0) ? v[i] + b : v[i];
       lg[i] = l;
-      key[i] = rank_key((bias && bias_mode == 1) ? l + b : l, e);
+      key[i] = score_key(select_bias ? l + b : l);
     }
   }
 
-  // softmax reference point: the largest logit (selection may use biased scores)
+  // softmax reference point: the largest logit -- round 0's score when the
+  // selection ranks the logits themselves, else a reduction of its own
   float m = -INFINITY;
+  if (score == 0 && select_bias) {
 #pragma unroll
-  for (int i = 0; i < NS; ++i) m = fmaxf(m, lg[i]);
-  m = wave_max(m);
+    for (int i = 0; i < NS; ++i) m = fmaxf(m, lg[i]);
+    m = wave_max(m);
+  }
 
-  float denom = 0.f, kth = 0.f;
+  uint32_t kth = 0u;
   int my_e = 0;
-  float my_p = 0.f;
+  float my_l = 0.f;
   for (int r = 0; r < k; ++r) {
-    unsigned long long best = 0ull;
+    uint32_t best = 0u;
 #pragma unroll
     for (int i = 0; i < NS; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    // every lane holds the same best: make it scalar (the builtin returns a
-    // signed int: each half goes through uint32_t, or the low half -- whose
-    // top bit is set for every expert index -- would sign-extend over the
-    // score in the high half)
-    best = ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(best >> 32))
-            << 32) |
-           (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)best);
-    const int e = (int)(0xffffffffu - (uint32_t)best);
+    best = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max_u32(best));
+    // this lane's lowest expert index holding that key (slots in ascending
+    // index order), 0xffffffff if none
+    uint32_t cand = 0xffffffffu;
+#pragma unroll
+    for (int i = NS - 1; i >= 0; --i)
+      if (key[i] == best) cand = (uint32_t)(lane + i * kWave);
+    const unsigned long long holders = __ballot(cand != 0xffffffffu);
+    uint32_t e;
+    if (__popcll(holders) == 1)
+      e = (uint32_t)__builtin_amdgcn_readlane((int)cand, __builtin_ctzll(holders));
+    else  // an equal score in several lanes
+      e = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min_u32(cand));
     const int owner = e & 63, slot = e >> 6;
     float l = 0.f;
 #pragma unroll
@@ -187,37 +179,39 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ part, int k
     if (lane == owner) {
 #pragma unroll
       for (int i = 0; i < NS; ++i)
-        if (i == slot) key[i] = 0ull;
+        if (i == slot) key[i] = 0u;
     }
-    const float p = score == 0 ? expf(l - m) : 1.f / (1.f + expf(-l));
-    denom += p;
+    if (r == 0 && score == 0 && !select_bias) m = l;
     if (lane == r) {
-      my_e = e;
-      my_p = p;
+      my_e = (int)e;
+      my_l = l;
     }
-    if (r == k - 1) kth = key_score(best);
+    kth = best;
   }
-  unsigned long long nxt = 0ull;
+  uint32_t nxt = 0u;
 #pragma unroll
   for (int i = 0; i < NS; ++i) nxt = key[i] > nxt ? key[i] : nxt;
-  nxt = wave_max_u64(nxt);
+  nxt = wave_max_u32(nxt);
 
-  if (!renorm) {
-    if (score == 0) {
-      float z = 0.f;
+  // the k scores side by side; their sum in round order
+  const float p = score == 0 ? expf(my_l - m) : 1.f / (1.f + expf(-my_l));
+  float denom = 0.f;
+  if (renorm) {
+    for (int r = 0; r < k; ++r) denom += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p), r));
+  } else if (score == 0) {
+    float z = 0.f;
 #pragma unroll
-      for (int i = 0; i < NS; ++i)
-        if (lane + i * kWave < E) z += expf(lg[i] - m);
-      denom = wave_sum(z);
-    } else {
-      denom = 1.f;
-    }
+    for (int i = 0; i < NS; ++i)
+      if (lane + i * kWave < E) z += expf(lg[i] - m);
+    denom = wave_sum(z);
+  } else {
+    denom = 1.f;
   }
   if (lane < k) {
     idx[(size_t)t * k + lane] = my_e;
-    wout[(size_t)t * k + lane] = my_p * (scale / denom);
+    wout[(size_t)t * k + lane] = p * (scale / denom);
   }
-  if (lane == 0) gap[t] = nxt ? kth - key_score(nxt) : INFINITY;
+  if (lane == 0) gap[t] = nxt ? key_score(kth) - key_score(nxt) : INFINITY;
 }
 
 }  // namespace moe

@@ -265,11 +265,51 @@ def test_graph_capture_replays(tokens, experts):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("tokens", [32, 1500])
+@pytest.mark.parametrize("fill", ["zeros", "ones", "ramp", "random"])
+def test_small_batch_workspace_of_any_contents(fill):
+    """No state carries over through the workspace: one holding zeros, all
+    ones, a ramp of 64-bit words or random bytes, and one last used by
+    batches of other sizes (other offsets for every buffer, the fused top-k +
+    dispatch's completion counter among them), give the output and routing of
+    a fresh workspace, bit for bit -- batches of 1 to 64 tokens, whose
+    dispatch runs on one wave."""
+    s = W["tiny"].replace(name="tiny_bf16_ws", act_dtype="bf16", tokens=64)
+    inp = moe_synth.make_layer(s, seed=8, device="cuda")
+    layer = make_layer(s)
+    layer.pack_inputs(inp)
+    sizes = (48, 17, 64, 1, 48, 48)
+    refs = {t: layer.forward(inp.x[:t].contiguous(), inp.router_w, return_route=True)
+            for t in set(sizes)}
+    torch.cuda.synchronize()
+    nbytes = max(layer.workspace_bytes(t) for t in sizes)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    if fill == "zeros":
+        ws.zero_()
+    elif fill == "ones":
+        ws.fill_(255)
+    elif fill == "ramp":
+        ws.view(torch.int64).copy_(torch.arange(nbytes // 8, dtype=torch.int64, device="cuda"))
+    else:
+        g = torch.Generator(device="cuda").manual_seed(11)
+        ws.copy_(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g))
+    for t in sizes:
+        out, route = layer.forward(inp.x[:t].contiguous(), inp.router_w, workspace=ws,
+                                   return_route=True)
+        torch.cuda.synchronize()
+        _say("workspace", fill, "tokens", t)
+        ref, rref = refs[t]
+        assert torch.equal(out, ref)
+        for name in ("topk_idx", "topk_w", "expert_counts", "expert_offsets", "perm", "inv"):
+            assert torch.equal(getattr(route, name), getattr(rref, name)), name
+
+
+@pytest.mark.parametrize("tokens", [32, 200, 1500])
 def test_timed_forward_matches(tokens):
     """The timed entry point runs the same kernels as the plain one (same
-    output bit for bit) and leaves five finite, positive stage durations, on a
-    fused-dispatch batch and on one with the multi-workgroup dispatch."""
+    output bit for bit) and leaves five finite, positive stage durations, on
+    batches whose fused top-k + dispatch ends in the one-wave dispatch (32
+    tokens) or the one-workgroup dispatch (200), and on one with the
+    multi-workgroup dispatch."""
     from sparse_mixture_experts_layer_amd import _binding as B
     s = W["tiny"].replace(name=f"tiny_bf16_timed_{tokens}", act_dtype="bf16", tokens=tokens)
     inp = moe_synth.make_layer(s, seed=6, device="cuda")
