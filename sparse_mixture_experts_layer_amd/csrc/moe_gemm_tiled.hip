@@ -46,12 +46,12 @@ namespace moe {
 namespace {
 
 constexpr int kTN = 256;                      // weight rows per tile
-constexpr int kStages = 3;
 constexpr int kBFrags = kTN / 16;             // 16
 constexpr int kXcds = 8;
 
 // Per tile height TM: waves, fragments per stage, loads per wave and stage.
-template <int TM>
+// NS: LDS ring stages (k-steps of loads in flight).
+template <int TM, int NS>
 struct TileShape {
   static constexpr int kWaves = TM / 32;                          // 4 or 8
   static constexpr int kAFrags = TM / 16;                         // 8 or 16
@@ -62,7 +62,8 @@ struct TileShape {
   // Y staging in the epilogue: MP fragment rows (16 rows each) per pass
   static constexpr int kMP = TM == 128 ? 2 : 1;
   static constexpr int kPitch = 128 * 4 + 16;                     // bytes per staged row
-  static_assert(kWaves * kMP * 16 * kPitch <= kStages * kStageBytes, "Y staging fits the ring");
+  static_assert(kWaves * kMP * 16 * kPitch <= NS * kStageBytes, "Y staging fits the ring");
+  static_assert(kWaves * 16 * kFragBytes <= NS * kStageBytes, "h staging fits the ring");
 };
 
 template <int MODE, int TM>
@@ -70,14 +71,18 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
                                                     const int32_t* __restrict__ row_tok,
                                                     void* __restrict__ out, int hstride,
                                                     uint16_t* __restrict__ h_lo, int nblk) {
-  using TS = TileShape<TM>;
+  // ring stages: 4 with 256-row tiles (down: 32 KiB stages, 128 KiB of ring;
+  // gate/up: 4 B slots of 16 KiB and 3 A double slots of 32 KiB, all 160 KiB
+  // of LDS), 3 with 128-row tiles
+  constexpr int kStages = TM == 256 ? 4 : 3;
+  using TS = TileShape<TM, kStages>;
   constexpr int kAFrags = TS::kAFrags, kStageBytes = TS::kStageBytes;
   constexpr int kAL = TS::kAL, kBL = TS::kBL, kLoadsPerStage = TS::kLoads;
   // Gate/up with 256-row tiles fetches the gathered x rows as whole 128-byte
   // lines: one wave-wide load takes 64 k of 8 rows (8 lanes per row) instead
   // of 32 k of 16 rows, which halves the cache lines each load touches.  A
-  // line spans two k-steps, so A sits in two double-step slots (TM rows x 64
-  // k each) beside a 3-slot ring of B; the 16-byte chunks of a row are
+  // line spans two k-steps, so A sits in kStages-1 double-step slots (TM rows
+  // x 64 k each) beside a kStages-slot ring of B; the 16-byte chunks of a row are
   // XOR-swizzled by the row's index within its 8-row block so that the MFMA
   // operand reads stay free of bank conflicts.  Every other kernel keeps A
   // and B together per k-step.
@@ -85,7 +90,8 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   constexpr int kBSlot = kBFrags * kFragBytes;                    // 16 KiB
   constexpr int kA2Bytes = TM * 128;                              // TM rows x 64 k
   constexpr int kA2Loads = kA2Bytes / kFragBytes / TS::kWaves;    // 4 per wave
-  constexpr int kLdsBytes = XL ? kStages * kBSlot + 2 * kA2Bytes : kStages * kStageBytes;
+  constexpr int kA2Slots = kStages - 1;
+  constexpr int kLdsBytes = XL ? kStages * kBSlot + kA2Slots * kA2Bytes : kStages * kStageBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
   // Work order.  Workgroups are dealt round-robin over the 8 XCDs (each with
@@ -267,9 +273,11 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
       load_frag<3 * kFragBytes>(gb, lb);
     }
   };
-  // XL: B of k-step kk in ring slot kk % 3; A of k-steps 2d, 2d+1 in double
-  // slot d % 2 (its slot is free once both steps were read, at the barrier of
-  // step 2d+1, which is when double step d+2 is issued)
+  // XL: B of k-step kk in ring slot kk % kStages; A of k-steps 2d, 2d+1 in
+  // double slot d % kA2Slots, issued with B of k-step 2d, kStages steps ahead
+  // (that slot's previous double step, d - kA2Slots, was last read in step
+  // 2d - kStages - 1, which every wave has left at the barrier of step
+  // 2d - kStages that issues it)
   auto issue_b = [&](int kk, int slot) {
     uint8_t* lb = lds + slot * kBSlot + kBL * wave * kFragBytes;
     const uint8_t* gb = bsrc + (size_t)kk * 4 * kFragBytes;
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   auto issue = [&](int kk) {
     if constexpr (XL) {
       issue_b(kk, kk % kStages);
-      if ((kk & 1) == 0) issue_a2(kk >> 1, (kk >> 1) & 1);
+      if ((kk & 1) == 0) issue_a2(kk >> 1, (kk >> 1) % kA2Slots);
     } else {
       issue_kstep(kk, kk % kStages);
     }
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
   const int xa = (xr >> 3) * kFragBytes + (xr & 7) * 128 + 16 * ((lane >> 4) ^ (xr & 7));
   auto rd_a = [&](int kk, int m) {
     const uint8_t* p =
-        XL ? lds + kStages * kBSlot + ((kk >> 1) & 1) * kA2Bytes + (wm * 4 + m) * 2 * kFragBytes +
+        XL ? lds + kStages * kBSlot + ((kk >> 1) % kA2Slots) * kA2Bytes + (wm * 4 + m) * 2 * kFragBytes +
                  (xa ^ ((kk & 1) * 64))
            : lds + (kk % kStages) * kStageBytes + (wm * 4 + m) * kFragBytes + lane * 16;
     return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
@@ -328,10 +336,10 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
 
   // Pipeline, per k-step kk: wait until stage kk+1 has landed (own loads:
   // vmcnt; everyone's: barrier), refill the ring slot of stage kk (already in
-  // registers) with stage kk+3, then run the MFMAs of stage kk while reading
-  // stage kk+1 from LDS into registers: each B fragment is re-read in place
-  // once its 4 MFMAs are issued, the A fragments go to a second register set.
-  // Global loads of two stages stay in flight.
+  // registers) with stage kk+kStages, then run the MFMAs of stage kk while
+  // reading stage kk+1 from LDS into registers: each B fragment is re-read in
+  // place once its 4 MFMAs are issued, the A fragments go to a second register
+  // set.  Global loads of kStages-1 stages stay in flight.
   bf16x8 a0[4], a1[4], b[8];
   auto step = [&](int kk, bf16x8(&ca)[4], bf16x8(&na)[4], bool do_issue, bool do_read, int vm) {
     wait_vm_lgkm0(vm);
@@ -348,12 +356,23 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     }
   };
   // loads issued after k-step kk+1's that may still be in flight at step kk:
-  // those of k-step kk+2 (kStages == 3), if it exists
-  static_assert(kStages == 3, "one k-step of loads in flight past the one awaited");
-  auto vm_at = [&](int kk) { return kk + 2 < nk ? loads_of(kk + 2) : 0; };
-  // the same in the main loop, for an even kk and for kk + 1
-  constexpr int kVmEven = XL ? kBL + kA2Loads : kLoadsPerStage;
-  constexpr int kVmOdd = XL ? kBL : kLoadsPerStage;
+  // those of k-steps kk+2 .. kk+kStages-1 that exist
+  auto vm_at = [&](int kk) {
+    int n = 0;
+#pragma unroll
+    for (int s = 2; s < kStages; ++s) n += kk + s < nk ? loads_of(kk + s) : 0;
+    return n;
+  };
+  // the same in the main loop, for an even kk and for kk + 1 (XL: an even
+  // k-step also carries a double step of A)
+  auto vm_main = [](int parity) {
+    int n = 0;
+    for (int s = 2; s < kStages; ++s)
+      n += XL ? kBL + (((parity + s) & 1) == 0 ? kA2Loads : 0) : kLoadsPerStage;
+    return n;
+  };
+  constexpr int kVmEven = vm_main(0);
+  constexpr int kVmOdd = vm_main(1);
 
   for (int pass = 0; pass < npass; ++pass) {
     // pass 1 (shared group, down GEMM) starts after the last step's barrier
@@ -458,31 +477,52 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
     return;
   }
   // packed h: row rr of row-block b, feature 32*blk + 16*f + c sits in
-  // fragment (b, blk) at lane rr + 16 * (2f + c/8), element c%8
+  // fragment (b, blk) at lane rr + 16 * (2f + c/8), element c%8.  The wave's
+  // 4 x 2 fragments (and their remainders, for the shared group) are put
+  // together in its own 16 KiB of the ring, idle since every wave passed the
+  // last k-step's barrier after its last LDS read, then stored whole: one
+  // 16-byte store per lane and fragment instead of 16 two-byte ones.  A
+  // fragment's rows past the tile are the group's padding rows (never stored
+  // by the down GEMM); fragments wholly past the tile are not stored.
+  uint16_t* sh = reinterpret_cast<uint16_t*>(lds + wave * 16 * kFragBytes);
+  uint16_t* sl = sh + 8 * (kFragBytes / 2);
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = (lane >> 4) * 4 + i;
-      const int r = wm * 64 + m * 16 + rr;
-      if (r >= nrows) continue;
-      const size_t b = (size_t)hb0 + wm * 4 + m, b_lo = (size_t)mt * (TM / 16) + wm * 4 + m;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const int blk = nb * 4 + wn * 2 + jb;
-        if (blk >= nblocks) continue;
+      for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const int in_frag = (rr + 16 * (2 * f + ((lane & 15) >> 3))) * 8 + (lane & 7);
+          const int at = (m * 2 + jb) * (kFragBytes / 2) +
+                         (rr + 16 * (2 * f + ((lane & 15) >> 3))) * 8 + (lane & 7);
           const float hv = swiglu(acc[m][jb * 4 + f][i], acc[m][jb * 4 + 2 + f][i], lim);
           const uint16_t hi = f32_to_bf16_bits(hv);
-          reinterpret_cast<uint16_t*>(out)[(b * hkb + blk) * (kFragBytes / 2) + in_frag] = hi;
-          if (shared)
-            h_lo[(b_lo * hkb + blk) * (kFragBytes / 2) + in_frag] =
-                f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
+          sh[at] = hi;
+          if (shared) sl[at] = f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
         }
-      }
     }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (wm * 64 + m * 16 >= nrows) continue;
+    const size_t b = (size_t)hb0 + wm * 4 + m, b_lo = (size_t)mt * (TM / 16) + wm * 4 + m;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int blk = nb * 4 + wn * 2 + jb;
+      if (blk >= nblocks) continue;
+      const int at = (m * 2 + jb) * (kFragBytes / 2) + lane * 8;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) +
+                                (b * hkb + blk) * (kFragBytes / 2) + lane * 8) =
+          *reinterpret_cast<const u32x4*>(sh + at);
+      if (shared)
+        *reinterpret_cast<u32x4*>(h_lo + (b_lo * hkb + blk) * (kFragBytes / 2) + lane * 8) =
+            *reinterpret_cast<const u32x4*>(sl + at);
+    }
+  }
 }
 
 // One thread per permuted row and 8 features: gate and up summed over the
