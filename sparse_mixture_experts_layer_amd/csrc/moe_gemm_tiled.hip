@@ -404,18 +404,50 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
 
   // epilogue: lane holds rows 4*(lane/16)+i of each 16-row fragment, column lane%16
   if (MODE == 1) {
-    // fp32 Y goes through LDS so that each lane stores 16 contiguous bytes and
-    // a wave writes whole 512-byte row segments (direct stores from the MFMA
-    // layout would write 64-byte pieces, 4 bytes per lane).  The ring is idle:
-    // every wave passed the last k-step's barrier after its last LDS read.
-    // Each wave stages its 64 x 128 block kMP fragment rows (16 rows each) at
-    // a time in a private region; rows are padded by 16 bytes against bank
-    // conflicts.
+    // Y goes through LDS so that each lane stores 16 contiguous bytes and a
+    // wave writes whole row segments (direct stores from the MFMA layout would
+    // write 64-byte pieces, 4 bytes per lane).  The ring is idle: every wave
+    // passed the last k-step's barrier after its last LDS read.  Each wave
+    // stages its 64 x 128 block kMP fragment rows (16 rows each) at a time in
+    // a private region; rows are padded by 16 bytes against bank conflicts.
     constexpr int kMP = TS::kMP, kPitch = TS::kPitch;
     uint8_t* stg = lds + wave * (kMP * 16 * kPitch);
     const int blk0 = nb * 4 + wn * 2;
-    // bf16 rows weighted by their gate weight at their pair's row (routed
-    // groups, no K split)
+    if (yb) {
+      // routed rows of bf16 Y: weighted by their gate weight and rounded in
+      // the MFMA layout (one shuffle per row for the weight), staged as bf16
+      // (rows of 128 values, padded by 16 bytes), then stored 16 bytes (8
+      // values) per lane at their pair's row
+      constexpr int kPB = 128 * 2 + 16;
+#pragma unroll
+      for (int pass = 0; pass < 4 / kMP; ++pass) {
+#pragma unroll
+        for (int mm = 0; mm < kMP; ++mm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int lr = mm * 16 + (lane >> 4) * 4 + i;
+            const float wr = __shfl(wrow, pass * kMP * 16 + lr);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              *reinterpret_cast<uint16_t*>(stg + lr * kPB + (j * 16 + (lane & 15)) * 2) =
+                  f32_to_bf16_bits(wr * acc[kMP * pass + mm][j][i]);
+          }
+        // kMP*16 rows x 16 chunks of 16 bytes, 64 chunks per wave-wide step
+#pragma unroll
+        for (int q = 0; q < kMP * 4; ++q) {
+          const int idx = q * kWave + lane, lr = idx >> 4, ch = idx & 15;
+          const int r = wm * 64 + pass * kMP * 16 + lr;
+          const int blk = blk0 + (ch >> 3);
+          const int pr = __shfl(prow, r - wm * 64);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + lr * kPB + ch * 16);
+          if (r < nrows && blk < nblocks)  // ordinary stores: 0.8% ahead of nontemporal ones
+            *reinterpret_cast<u32x4*>(g.yb + (size_t)pr * H + (size_t)blk * 64 + (ch & 7) * 8) = v;
+        }
+      }
+      return;
+    }
+    // fp32 rows: the shared group's (by token) or every row's (K-split planes,
+    // fp32 activations)
 #pragma unroll
     for (int pass = 0; pass < 4 / kMP; ++pass) {
 #pragma unroll
@@ -434,20 +466,13 @@ __global__ __launch_bounds__(TM * 2, TM == 128 ? 2 : 1) void tiled_kernel(GemmGe
         const f32x4 val = *reinterpret_cast<const f32x4*>(stg + lr * kPitch + ch * 16);
         const int r = wm * 64 + pass * kMP * 16 + lr;
         const int blk = blk0 + (ch >> 4);
-        const float wr = __shfl(wrow, r - wm * 64);
-        const int pr = __shfl(prow, r - wm * 64);
         const size_t col = (size_t)blk * 64 + (ch & 15) * 4;
-        if (r < nrows && blk < nblocks) {  // ordinary stores: 0.8% ahead of nontemporal ones
-          if (yb) {
-            const u32x2 pk = {pack_bf16x2(wr * val[0], wr * val[1]),
-                              pack_bf16x2(wr * val[2], wr * val[3])};
-            *reinterpret_cast<u32x2*>(g.yb + (size_t)pr * H + col) = pk;
-          } else if (g.y_bf16) {  // the shared group: fp32 rows by token
+        if (r < nrows && blk < nblocks) {
+          if (g.y_bf16)
             *reinterpret_cast<f32x4*>(g.ys + (size_t)(row0 + r - g.offsets[g.E]) * H + col) = val;
-          } else {
+          else
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + split * g.y_plane +
                                       (size_t)(row0 + r) * H + col) = val;
-          }
         }
       }
     }
