@@ -29,20 +29,21 @@ constexpr int kFragBytes = 1024;   // one 16x32 bf16 fragment
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 512;
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (NaN to a quiet NaN): gfx950's
+// v_cvt_pk_bf16_f32, two values per instruction (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
@@ -66,11 +67,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ void split_f32x8(const float* x, u32x4& hi, u32x4& lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint16_t h0 = f32_to_bf16_bits(x[2 * i]);
-    uint16_t h1 = f32_to_bf16_bits(x[2 * i + 1]);
-    float r0 = x[2 * i] - bf16_bits_to_f32(h0);
-    float r1 = x[2 * i + 1] - bf16_bits_to_f32(h1);
-    hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    const uint32_t h = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    const float r0 = x[2 * i] - __uint_as_float(h << 16);
+    const float r1 = x[2 * i + 1] - __uint_as_float(h & 0xffff0000u);
+    hi[i] = h;
     lo[i] = pack_bf16x2(r0, r1);
   }
 }
