@@ -79,18 +79,24 @@ struct TileInfo {
 };
 
 __device__ __forceinline__ bool tile_info(const GemmGeom& g, int tile, TileInfo& ti) {
-  if (tile >= *g.ntiles) return false;
+  // The entry is read alongside the tile count (tile < max_tiles: in bounds;
+  // an entry past the count is never used), then the group's offset alongside
+  // its count: two dependent scalar round trips before the first weight loads
+  // instead of four.
+  const int nt = *g.ntiles;
   const int v = g.tiles[tile];
-  ti.group = tile_group(v);
-  if (MOE_DEBUG && (ti.group < 0 || ti.group > g.E)) {  // never written by the dispatch
-    dbg_check(g.dbg, false, kDbgTile, v);
+  const int grp = tile_group(v);
+  if (tile >= nt || grp < 0 || grp > g.E) {  // never a bad group below the count
+    if (MOE_DEBUG && tile < nt) dbg_check(g.dbg, false, kDbgTile, v);
     return false;
   }
   const int bm = 16 * g.tg;
   const int m = tile_m(v);
-  ti.row0 = g.offsets[ti.group] + m * bm;
-  ti.nrows = min(bm, g.counts[ti.group] - m * bm);
-  ti.width = ti.group == g.E ? g.Is : g.I;
+  const int off = g.offsets[grp], cnt = g.counts[grp];
+  ti.group = grp;
+  ti.row0 = off + m * bm;
+  ti.nrows = min(bm, cnt - m * bm);
+  ti.width = grp == g.E ? g.Is : g.I;
   return ti.nrows > 0;
 }
 
